@@ -1,0 +1,271 @@
+"""Benchmark of the sparse-index hot path on one MI355X.
+
+A step is one pass of the whole path over the 200K-token prefill workload:
+25 chunks of up to 8192 query rows against the resident keys, each chunk
+through run_layer_group with 4 layers F,S,S,S (indexer score + top-k in the F
+layer, index-cache reuse, sparse attention in every layer).
+
+Headline metric: indexer + top-k prefill query-tok/s at 200K context =
+200000 / (indexer time per step), where the indexer time is the sum over
+chunks of the F layer's score + select kernels, timed with HIP events that
+run_layer_group records on the launch stream.  The JSON line also carries the
+whole-path rate, the FSSS vs all-F speedup (one all-F pass after the timed
+steps), the score kernel's MFMA roofline and the CPU oracle's rate on a
+bounded sample of rows.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from long_context_sparse_idx_amd import inputs, lcsi  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Path:
+    """Device-resident inputs and outputs of one workload."""
+
+    def __init__(self, wl, all_f_inputs: bool):
+        self.wl = wl
+        dev = "cuda"
+        L = wl.n_layers
+        self.f_layers = [l for l in range(L) if wl.pattern[l]]
+        need_f = list(range(L)) if all_f_inputs else self.f_layers
+        t0 = time.time()
+        self.idx_in = {l: inputs.indexer_inputs(wl, l, dev) for l in need_f}
+        self.attn_in = [inputs.attn_inputs(wl, l, dev) for l in range(L)]
+        self.outs = [torch.empty((wl.B, wl.n_q, wl.H_q, wl.D_v), dtype=torch.bfloat16, device=dev)
+                     for _ in range(L)]
+        self.cache = torch.empty((1, wl.B, wl.n_q, wl.top_k), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        log(f"[bench] inputs for {wl.name} ready in {time.time() - t0:.1f}s")
+        self.tau = inputs.sm_scale(wl)
+        self.ws = None
+        self.ws_bytes = 0
+
+    def chunk_descs(self, q0, tq, T_kv, pattern):
+        wl = self.wl
+        f_idx = [l for l in range(len(pattern)) if pattern[l]]
+        ids = []
+        for l in f_idx:
+            x = self.idx_in[l]
+            ids.append(lcsi.indexer_desc(x["q"][:, q0 - wl.q_pos0:q0 - wl.q_pos0 + tq], x["k"],
+                                         x["w"][:, q0 - wl.q_pos0:q0 - wl.q_pos0 + tq], wl.top_k, q0,
+                                         k_scale=x["k_scale"], T_kv=T_kv))
+        ads = []
+        for l in range(len(pattern)):
+            x = self.attn_in[l]
+            r0 = q0 - wl.q_pos0
+            ads.append(lcsi.attn_desc(x["q"][:, r0:r0 + tq], x["k"], x["v"], self.outs[l][:, r0:r0 + tq],
+                                      wl.top_k, q0, self.tau, T_kv=T_kv))
+        return ids, ads
+
+    def plan(self, pattern):
+        """Per-chunk descriptors and the shared workspace."""
+        wl = self.wl
+        plans = []
+        need = 0
+        for (q0, tq, T_kv) in wl.chunks():
+            ids, ads = self.chunk_descs(q0, tq, T_kv, pattern)
+            cache = self.cache[:, :, q0 - wl.q_pos0:]
+            n = lcsi.layer_group_ws_bytes(pattern, ids, ads, cache, 1, 0, wl.n_q * wl.top_k, wl.top_k)
+            need = max(need, n)
+            plans.append((q0, tq, T_kv, ids, ads, cache))
+        if need > self.ws_bytes:
+            self.ws = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+            self.ws_bytes = need
+        return plans
+
+    def step(self, pattern, plans, events=None):
+        wl = self.wl
+        for c, (q0, tq, T_kv, ids, ads, cache) in enumerate(plans):
+            ev = events[c] if events is not None else None
+            lcsi.run_layer_group(pattern, ids, ads, cache, 1, 0, wl.n_q * wl.top_k, wl.top_k,
+                                 ws=self.ws, events=ev)
+
+
+def pairs_in_chunk(q0, tq):
+    """Causal (query, key) pairs of rows q0 .. q0+tq-1."""
+    return tq * (q0 + 1) + tq * (tq - 1) // 2
+
+
+def cpu_baseline(path: Path, max_rows: int | None = None):
+    """The oracle's indexer + top-k on a bounded, evenly spaced sample of rows."""
+    import oracle
+    wl = path.wl
+    threads = oracle.default_threads()
+    R = max_rows or max(4, 2 * threads)
+    pos = np.array([wl.q_pos0 + int((i + 0.5) * wl.n_q / R) for i in range(R)], np.int64)
+    l = path.f_layers[0]
+    x = path.idx_in[l]
+    rows = torch.from_numpy(pos - wl.q_pos0).cuda()
+    q = x["q"][0].index_select(0, rows).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    w = x["w"][0].index_select(0, rows).cpu().numpy()
+    if wl.key_fp8:
+        keys = x["k"][0].cpu().numpy()
+        ks = x["k_scale"][0].cpu().numpy()
+    else:
+        keys = x["k"][0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        ks = None
+    t0 = time.time()
+    oracle.score_select(q, w, keys, pos, wl.top_k, k_scale=ks, want_scores=False, threads=threads)
+    dt = time.time() - t0
+    return {"value": R / dt, "unit": "query-tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{R} evenly spaced rows of the {wl.name} workload (positions {pos[0]}..{pos[-1]}), "
+                      f"indexer score + top-k, {dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="prefill200k", choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-allf", action="store_true", help="skip the all-F comparison pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
+              "multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    wl = inputs.WORKLOADS[args.workload]
+    path = Path(wl, all_f_inputs=not args.no_allf)
+    pattern = wl.pattern
+    plans = path.plan(pattern)
+    L = wl.n_layers
+    nchunk = len(plans)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] for _ in range(nchunk)]
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        path.step(pattern, plans)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ms, idx_ms, score_ms, select_ms, attn_ms = [], [], [], [], []
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        path.step(pattern, plans, events)
+        torch.cuda.synchronize()
+        sc = se = at = 0.0
+        for c in range(nchunk):
+            ev = events[c]
+            for l in range(L):
+                sc += ev[4 * l].elapsed_time(ev[4 * l + 1])
+                se += ev[4 * l + 1].elapsed_time(ev[4 * l + 2])
+                at += ev[4 * l + 2].elapsed_time(ev[4 * l + 3])
+        step_ms.append(s0.elapsed_time(events[-1][-1]))
+        score_ms.append(sc)
+        select_ms.append(se)
+        attn_ms.append(at)
+        idx_ms.append(sc + se)
+        log(f"[bench] step {i + 1}/{args.steps}: {step_ms[-1]:.1f} ms (score {sc:.1f}, select {se:.1f}, "
+            f"attention {at:.1f})")
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+
+    n_q_total = wl.B * wl.n_q
+    ms_step = total_ms / args.steps
+    idx_mean = float(np.mean(idx_ms))
+    value = n_q_total / (idx_mean / 1e3)
+
+    # roofline of the dominant kernel (indexer score, MFMA-bound in prefill)
+    pairs = sum(pairs_in_chunk(q0, tq) for (q0, tq, _, _, _, _) in plans) * wl.B
+    flops_per_pair = 2 * wl.H_I * wl.D_I
+    n_f = sum(pattern)
+    score_s = float(np.mean(score_ms)) / 1e3
+    achieved = pairs * flops_per_pair * n_f / score_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "score_prefill_kernel<64,128,bf16>",
+                "launches_per_step": nchunk * n_f,
+                "avg_launch_ms": round(float(np.mean(score_ms)) / (nchunk * n_f), 4)}
+    # select: HBM-bound; algorithmic bytes = read each causal score once + write k indices
+    sel_bytes = (pairs * 4 + n_q_total * wl.top_k * 4) * n_f
+    sel_gbs = sel_bytes / (float(np.mean(select_ms)) / 1e3) / 1e9
+    # attention: bytes of the gathered KV rows (576 x bf16 per selected index) + Q + O
+    sel_per_row = sum(min(wl.top_k, p + 1) for p in range(wl.q_pos0, wl.q_pos0 + wl.n_q)) * wl.B
+    attn_bytes = (sel_per_row * wl.D_qk * 2 + n_q_total * wl.H_q * (wl.D_qk + wl.D_v) * 2) * L
+    attn_gbs = attn_bytes / (float(np.mean(attn_ms)) / 1e3) / 1e9
+
+    extra = {}
+    if not args.no_allf:
+        allf = tuple(1 for _ in range(L))
+        plans_f = path.plan(allf)
+        path.step(allf, plans_f)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev_f = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] for _ in range(nchunk)]
+        e0.record(stream)
+        path.step(allf, plans_f, ev_f)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        allf_ms = e0.elapsed_time(e1)
+        idx_f = sum(ev[4 * l].elapsed_time(ev[4 * l + 2]) for ev in ev_f for l in range(L))
+        extra["allF_ms_per_step"] = round(allf_ms, 2)
+        extra["fsss_speedup_vs_allF"] = round(allf_ms / float(np.mean(step_ms)), 3)
+        extra["indexer_share_allF"] = round(idx_f / allf_ms, 3)
+        extra["indexer_share_fsss"] = round(idx_mean / float(np.mean(step_ms)), 3)
+        log(f"[bench] all-F pass: {allf_ms:.1f} ms")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(path)
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} ({cpu['sample']})")
+
+    line = {
+        "metric": "indexer+top-k prefill query-tok/s at 200K ctx" if wl.name == "prefill200k"
+        else f"indexer+top-k query-tok/s ({wl.name})",
+        "value": round(value, 1),
+        "unit": "query-tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not wl.key_fp8 else "bf16 (fp8 e4m3 keys widened exactly)",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.q_pos0 + wl.n_q, "B": wl.B, "chunk": wl.T_q,
+                   "pattern": "".join("F" if f else "S" for f in pattern), "H_I": wl.H_I,
+                   "D_I": wl.D_I, "top_k": wl.top_k, "H_q": wl.H_q, "D_qk": wl.D_qk, "D_v": wl.D_v},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "path_query_tok_s": round(n_q_total / (float(np.mean(step_ms)) / 1e3), 1),
+        "ms": {"score": round(float(np.mean(score_ms)), 3), "select": round(float(np.mean(select_ms)), 3),
+               "attention": round(float(np.mean(attn_ms)), 3), "indexer": round(idx_mean, 3),
+               "step_events": round(float(np.mean(step_ms)), 3)},
+        "select_algorithmic_GBps": round(sel_gbs, 1),
+        "attention_algorithmic_GBps": round(attn_gbs, 1),
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

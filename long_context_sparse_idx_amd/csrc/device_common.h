@@ -1,0 +1,88 @@
+// Device-side helpers shared by the gfx950 kernels of liblcsi.
+// Wave64 only: every helper assumes 64 lanes per wavefront.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcsi {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Number of set bits of `mask` strictly below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// OCP E4M3 (fn variant) byte -> bf16 bits, exact for every finite code.
+// Normal codes (exponent field e >= 1): value (1 + m/8) 2^(e-7) keeps its
+// 3 mantissa bits and rebiases the exponent by 127 - 7 = 120.  Subnormal
+// codes (e == 0): value m * 2^-9, formed exactly through fp32.
+__device__ __forceinline__ uint32_t fp8e4m3_to_bf16_bits(uint32_t b)
+{
+    uint32_t em = b & 0x7Fu;
+    uint32_t r = em >= 8u ? (em << 4) + (120u << 7)
+                          : (__float_as_uint((float)em * 0x1p-9f) >> 16);
+    return r | ((b & 0x80u) << 8);
+}
+
+// Four fp8 bytes (one dword) -> four bf16 values packed in two dwords.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w)
+{
+    u32x2 r;
+    r.x = fp8e4m3_to_bf16_bits(w & 0xFFu) | (fp8e4m3_to_bf16_bits((w >> 8) & 0xFFu) << 16);
+    r.y = fp8e4m3_to_bf16_bits((w >> 16) & 0xFFu) | (fp8e4m3_to_bf16_bits(w >> 24) << 16);
+    return r;
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 is
+// mapped like +0 so the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace lcsi

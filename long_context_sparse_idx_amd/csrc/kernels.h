@@ -1,0 +1,63 @@
+// Internal launch interface between the C-ABI host code (api.hip) and the
+// kernels.  Not installed; the public interface is include/lcsi.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcsi {
+
+struct ScoreArgs {
+    int B, T_q, T_kv, H, D;
+    int fp8;
+    int64_t q_pos0;
+    const uint16_t *q;        // bf16, strides in elements
+    int64_t q_sb, q_st, q_sh;
+    const uint8_t *k;         // bf16 or fp8 rows, strides in BYTES
+    int64_t k_sb, k_st;
+    const float *k_scale;     // fp8 only
+    int64_t ks_sb;
+    const float *w;
+    int64_t w_sb, w_st;
+    float *S;                 // [B][T_q][ld]
+    int64_t ld;
+    int key_split;            // keys per workgroup (split-key kernel)
+};
+
+struct SelectArgs {
+    int B, T_q, top_k;
+    int64_t q_pos0, T_kv;
+    const float *S;           // [B][T_q][ld]
+    int64_t ld;
+    int32_t *idx;
+    int64_t idx_sb, idx_st;
+};
+
+struct AttnArgs {
+    int B, T_q, T_kv, H, DQK, DV, top_k;
+    float sm_scale_log2;      // sm_scale * log2(e)
+    int64_t q_pos0;
+    const uint16_t *q;
+    int64_t q_sb, q_st, q_sh;
+    const uint16_t *k;
+    int64_t k_sb, k_st;
+    const uint16_t *v;
+    int64_t v_sb, v_st;
+    uint16_t *out;
+    int64_t o_sb, o_st, o_sh;
+    const int32_t *idx;
+    int64_t idx_sb, idx_st;
+    int splits;               // key splits per query row (1 = write bf16 directly)
+    int split_len;            // index entries per split (multiple of 32)
+    float *part_o;            // [B*T_q][splits][H][DV] (splits > 1)
+    float *part_ml;           // [B*T_q][splits][H][2]
+};
+
+bool score_use_split(const ScoreArgs &a);
+int score_key_split(const ScoreArgs &a);
+hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
+hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len);
+hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
+
+}  // namespace lcsi

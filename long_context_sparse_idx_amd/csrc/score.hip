@@ -1,0 +1,361 @@
+// Indexer score kernels for gfx950.
+//
+//   S[b,t,s] = sum_h w[b,t,h] * max(0, q[b,t,h,:] . k[b,s,:])   for s <= p_t
+//
+// (The pages name the indexer only as a dot product followed by a top-k --
+// IndexShare term page (earlyterms.com), opening definition -- and place it
+// in front of every layer's attention, scanning the whole context --
+// IndexCache news article (app.myzaker.com), section "IndexCache".)
+//
+// The contraction over d is dense, so it runs on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16).  A wave owns 64 "rows" = (query, head) pairs
+// with heads contiguous (64/H queries per wave) as the MFMA M dimension, keys
+// are the N dimension (32 per block), d is K.  The ReLU, the per-head weight
+// and the head reduction run in the epilogue on the fp32 accumulators, so
+// per-head scores never leave registers; only the head-reduced row is
+// written (fp32, one row of ld floats per query).
+//
+// fp8 keys: every OCP E4M3 value is exactly a bf16 value, so keys are widened
+// to bf16 on load and the per-key scale is applied after the head reduction
+// (max(0, a x) = a max(0, x) for a > 0).
+//
+// Lane layouts (32x32x16 bf16 MFMA, wave64, g = lane / 32):
+//   A (Q):  lane holds row (lane % 32), 8 consecutive k-slots of group g
+//   B (K):  lane holds column (lane % 32), the same 8 k-slots of group g
+//   D:      lane holds column (lane % 32), rows 8*(r/4) + 4*g + (r%4), r < 16
+// The d index behind k-slot e of group g in k-step s is g*D/2 + 8*s + e: both
+// operands use the same map, so the MFMA still sums all D products, and each
+// lane reads one contiguous half of a row (128 B for D = 128).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace lcsi {
+
+namespace {
+
+constexpr int WAVES_PREFILL = 8;  // 512 threads: 2 waves per SIMD
+constexpr int WAVES_SPLIT = 4;
+constexpr int KT = 64;            // keys per LDS tile (two 32-key MFMA blocks)
+
+template <int D>
+struct KeyGeom {
+    static constexpr int KSTEPS = D / 16;     // MFMA k-steps
+    static constexpr int HALF = D / 2;        // d-elements per lane group
+    static constexpr int ROWB = D * 2 + 16;   // LDS bytes per bf16 key row (+16 B pad)
+};
+
+// Q fragments and per-row weights of one wave (64 rows = 64/H queries).
+template <int H, int D>
+struct WaveRows {
+    bf16x8 qa[2][KeyGeom<D>::KSTEPS];
+    float wl[2][16];
+
+    __device__ __forceinline__ void load(const ScoreArgs &a, int b, int tq0, int lane)
+    {
+        const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int row = rt * 32 + l32;
+            const int t = tq0 + row / H, h = row % H;
+            if (t < a.T_q) {
+                const uint16_t *base = a.q + b * a.q_sb + (int64_t)t * a.q_st + h * a.q_sh + g * KeyGeom<D>::HALF;
+#pragma unroll
+                for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(ld16(base + 8 * s));
+            } else {
+#pragma unroll
+                for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = rt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const int tr = tq0 + rr / H, hr = rr % H;
+                wl[rt][r] = tr < a.T_q ? a.w[b * a.w_sb + (int64_t)tr * a.w_st + hr] : 0.f;
+            }
+        }
+    }
+};
+
+// ReLU * weight, head reduction and the store of one 32-key block.
+// Summation order is fixed (rt, then r ascending, then the lane-pair add),
+// so every kernel that calls this produces bit-identical scores.
+template <int H>
+__device__ __forceinline__ void score_epilogue(const f32x16 &acc0, const f32x16 &acc1, const float (&wl)[2][16],
+                                               float kscale, float *Sb, int64_t ld, int T_q, int tq0, int key,
+                                               int lane)
+{
+    const int g = lane >> 5;
+    if constexpr (H >= 8) {
+        constexpr int QPW = 64 / H;
+        float part[QPW];
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) part[q] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[(8 * (r >> 2)) / H] += wl[0][r] * fmaxf(acc0[r], 0.f);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[(32 + 8 * (r >> 2)) / H] += wl[1][r] * fmaxf(acc1[r], 0.f);
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) part[q] = (part[q] + __shfl_xor(part[q], 32)) * kscale;
+        if constexpr (QPW == 1) {
+            if (g == 0 && tq0 < T_q) Sb[(int64_t)tq0 * ld + key] = part[0];
+        } else {
+#pragma unroll
+            for (int q = 0; q < QPW; ++q) {
+                const bool mine = (q < QPW / 2) == (g == 0);
+                const int t = tq0 + q;
+                if (mine && t < T_q) Sb[(int64_t)t * ld + key] = part[q];
+            }
+        }
+    } else {
+        static_assert(H == 4, "H must be 4, 8, 16, 32 or 64");
+        // rows 8j + 4g + i (i < 4) of tile rt are the 4 heads of query 8*rt + 2j + g
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x16 &acc = rt == 0 ? acc0 : acc1;
+                float v = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v += wl[rt][4 * j + i] * fmaxf(acc[4 * j + i], 0.f);
+                const int t = tq0 + rt * 8 + 2 * j + g;
+                if (t < T_q) Sb[(int64_t)t * ld + key] = v * kscale;
+            }
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&qa)[2][KeyGeom<D>::KSTEPS], const bf16x8 (&bk)[KeyGeom<D>::KSTEPS],
+                                           f32x16 &acc0, f32x16 &acc1)
+{
+    acc0 = f32x16{0};
+    acc1 = f32x16{0};
+#pragma unroll
+    for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], bk[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], bk[s], acc1, 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup = 8 waves = 8*64/H consecutive query rows of one
+// sequence, sweeping keys 0 .. p_max in 64-key tiles staged (as bf16) in a
+// double-buffered LDS ring; the next tile is fetched into registers while the
+// current one feeds the MFMAs.  Workgroups are issued heaviest (last rows)
+// first.  All concurrently running workgroups sweep the keys in the same
+// order, so each XCD's L2 serves a key tile to all its workgroups.
+// ---------------------------------------------------------------------------
+template <int H, int D, bool FP8>
+__global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(ScoreArgs a)
+{
+    using G = KeyGeom<D>;
+    constexpr int QPW = 64 / H;
+    constexpr int QPB = WAVES_PREFILL * QPW;
+    constexpr int NT = WAVES_PREFILL * 64;
+    // 16-byte chunks of one tile as stored in LDS (bf16) and as read from HBM
+    constexpr int SRC_CHUNK_KEY = FP8 ? D / 16 : D / 8;   // per key
+    constexpr int SRC_CHUNKS = KT * SRC_CHUNK_KEY;
+    constexpr int CPT = (SRC_CHUNKS + NT - 1) / NT;
+
+    __shared__ __attribute__((aligned(16))) uint8_t sk[2][KT * G::ROWB];
+    __shared__ float ssc[2][KT];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int b = blockIdx.y;
+    const int t0 = (gridDim.x - 1 - blockIdx.x) * QPB;
+    const int t_end = min(a.T_q, t0 + QPB);
+    const int64_t n_keys = a.q_pos0 + t_end;
+    const int ntiles = (int)((n_keys + KT - 1) / KT);
+    const uint8_t *kb = a.k + b * a.k_sb;
+
+    WaveRows<H, D> rows;
+    const int tq0 = t0 + wave * QPW;
+    rows.load(a, b, tq0, lane);
+
+    u32x4 pf[CPT];
+    float pfs = 1.f;
+    auto fetch = [&](int tile) {
+        const int64_t key0 = (int64_t)tile * KT;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
+            const int64_t key = key0 + kk;
+            pf[i] = u32x4{0, 0, 0, 0};
+            if (c < SRC_CHUNKS && key < n_keys) pf[i] = ld16(kb + key * a.k_st + part * 16);
+        }
+        if constexpr (FP8) {
+            const int64_t key = key0 + tid;
+            pfs = (tid < KT && key < n_keys) ? a.k_scale[b * a.ks_sb + key] : 1.f;
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            if (c >= SRC_CHUNKS) break;
+            const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
+            uint8_t *dst = sk[buf] + kk * G::ROWB;
+            if constexpr (FP8) {
+                // 16 fp8 bytes -> 16 bf16 (32 bytes)
+                u32x2 lo0 = fp8x4_to_bf16x4(pf[i].x), lo1 = fp8x4_to_bf16x4(pf[i].y);
+                u32x2 hi0 = fp8x4_to_bf16x4(pf[i].z), hi1 = fp8x4_to_bf16x4(pf[i].w);
+                st16(dst + part * 32, u32x4{lo0.x, lo0.y, lo1.x, lo1.y});
+                st16(dst + part * 32 + 16, u32x4{hi0.x, hi0.y, hi1.x, hi1.y});
+            } else {
+                st16(dst + part * 16, pf[i]);
+            }
+        }
+        if constexpr (FP8) {
+            if (tid < KT) ssc[buf][tid] = pfs;
+        }
+    };
+
+    float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntiles) fetch(it + 1);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const uint8_t *src = sk[buf] + (cb * 32 + l32) * G::ROWB + g * G::HALF * 2;
+            bf16x8 bk[G::KSTEPS];
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
+            f32x16 acc0, acc1;
+            mfma_block<D>(rows.qa, bk, acc0, acc1);
+            const float ksc = FP8 ? ssc[buf][cb * 32 + l32] : 1.f;
+            score_epilogue<H>(acc0, acc1, rows.wl, ksc, Sb, a.ld, a.T_q, tq0, it * KT + cb * 32 + l32, lane);
+        }
+        if (it + 1 < ntiles) stash(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split-key variant for few query rows (decode): a workgroup takes one group
+// of 64/H query rows and a contiguous key range; its 4 waves stride over the
+// 32-key blocks of that range, reading key fragments straight from HBM with
+// the next block's loads in flight while the current block computes.
+// ---------------------------------------------------------------------------
+template <int H, int D, bool FP8>
+__global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreArgs a)
+{
+    using G = KeyGeom<D>;
+    constexpr int QPW = 64 / H;
+    // per lane: G::HALF key elements = HALF*2 bytes (bf16) or HALF bytes (fp8)
+    constexpr int NLD = FP8 ? G::HALF / 16 : G::HALF / 8;  // 16-byte loads per lane per block
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int b = blockIdx.z;
+    const int tq0 = blockIdx.y * QPW;
+    const int64_t n_keys = a.q_pos0 + min(a.T_q, tq0 + QPW);
+    const int64_t key_lo = (int64_t)blockIdx.x * a.key_split;
+    const int64_t key_hi = min<int64_t>(n_keys, key_lo + a.key_split);
+    if (key_lo >= key_hi) return;
+    const int nblk = (int)((key_hi - key_lo + 31) / 32);
+
+    WaveRows<H, D> rows;
+    rows.load(a, b, tq0, lane);
+    const uint8_t *kb = a.k + b * a.k_sb;
+    float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
+
+    u32x4 cur[NLD], nxt[NLD];
+    float cs = 1.f, ns = 1.f;
+    auto fetch = [&](int blk, u32x4 (&r)[NLD], float &sc) {
+        const int64_t key = key_lo + (int64_t)blk * 32 + l32;
+        const bool ok = blk < nblk && key < key_hi;
+        const uint8_t *src = kb + key * a.k_st + g * (FP8 ? G::HALF : G::HALF * 2);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) r[i] = ok ? ld16(src + 16 * i) : u32x4{0, 0, 0, 0};
+        if constexpr (FP8) sc = ok ? a.k_scale[b * a.ks_sb + key] : 1.f;
+    };
+
+    int blk = wave;
+    fetch(blk, cur, cs);
+    for (; blk < nblk; blk += WAVES_SPLIT) {
+        fetch(blk + WAVES_SPLIT, nxt, ns);
+        bf16x8 bk[G::KSTEPS];
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                u32x2 p0 = fp8x4_to_bf16x4(cur[i].x), p1 = fp8x4_to_bf16x4(cur[i].y);
+                u32x2 p2 = fp8x4_to_bf16x4(cur[i].z), p3 = fp8x4_to_bf16x4(cur[i].w);
+                bk[2 * i] = as_bf16x8(u32x4{p0.x, p0.y, p1.x, p1.y});
+                bk[2 * i + 1] = as_bf16x8(u32x4{p2.x, p2.y, p3.x, p3.y});
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) bk[i] = as_bf16x8(cur[i]);
+        }
+        f32x16 acc0, acc1;
+        mfma_block<D>(rows.qa, bk, acc0, acc1);
+        const int64_t key = key_lo + (int64_t)blk * 32 + l32;
+        score_epilogue<H>(acc0, acc1, rows.wl, cs, Sb, a.ld, a.T_q, tq0, (int)key, lane);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) cur[i] = nxt[i];
+        cs = ns;
+    }
+}
+
+template <int H, int D, bool FP8>
+hipError_t launch_score_hd(const ScoreArgs &a, bool split, hipStream_t st)
+{
+    constexpr int QPW = 64 / H;
+    if (!split) {
+        constexpr int QPB = WAVES_PREFILL * QPW;
+        dim3 grid((a.T_q + QPB - 1) / QPB, a.B);
+        hipLaunchKernelGGL((score_prefill_kernel<H, D, FP8>), grid, dim3(WAVES_PREFILL * 64), 0, st, a);
+    } else {
+        const int64_t n_keys = a.q_pos0 + a.T_q;
+        dim3 grid((unsigned)((n_keys + a.key_split - 1) / a.key_split), (a.T_q + QPW - 1) / QPW, a.B);
+        hipLaunchKernelGGL((score_splitkey_kernel<H, D, FP8>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <int H>
+hipError_t launch_score_h(const ScoreArgs &a, bool split, hipStream_t st)
+{
+    if (a.D == 128) return a.fp8 ? launch_score_hd<H, 128, true>(a, split, st) : launch_score_hd<H, 128, false>(a, split, st);
+    return a.fp8 ? launch_score_hd<H, 64, true>(a, split, st) : launch_score_hd<H, 64, false>(a, split, st);
+}
+
+}  // namespace
+
+// Heuristic: the LDS-staged prefill kernel when there are enough query rows
+// to fill the chip, the split-key kernel otherwise.  Both give identical bits.
+bool score_use_split(const ScoreArgs &a)
+{
+    const int qpb = WAVES_PREFILL * (64 / a.H);
+    const int64_t blocks = (int64_t)a.B * ((a.T_q + qpb - 1) / qpb);
+    return blocks < 256 && (a.q_pos0 + a.T_q) >= 4096;
+}
+
+int score_key_split(const ScoreArgs &a)
+{
+    // aim for >= ~1024 workgroups; keep ranges a multiple of 32 keys
+    const int64_t n_keys = a.q_pos0 + a.T_q;
+    const int64_t groups = (int64_t)a.B * ((a.T_q + 64 / a.H - 1) / (64 / a.H));
+    int64_t splits = (1024 + groups - 1) / groups;
+    int64_t ks = (n_keys + splits - 1) / splits;
+    ks = ((ks + 255) / 256) * 256;
+    if (ks < 512) ks = 512;
+    return (int)ks;
+}
+
+hipError_t launch_score(const ScoreArgs &a, hipStream_t st)
+{
+    const bool split = score_use_split(a);
+    switch (a.H) {
+    case 4: return launch_score_h<4>(a, split, st);
+    case 8: return launch_score_h<8>(a, split, st);
+    case 16: return launch_score_h<16>(a, split, st);
+    case 32: return launch_score_h<32>(a, split, st);
+    case 64: return launch_score_h<64>(a, split, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lcsi

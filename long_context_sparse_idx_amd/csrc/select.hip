@@ -1,0 +1,343 @@
+// Per-row top-k selection for gfx950 (the second half of the indexer's
+// "dot product + top-k": IndexShare term page (earlyterms.com), opening
+// definition; each token keeps its top-k positions: IndexShare explainer
+// (yun88.com), section on the hidden indexer cost).
+//
+// Row p holds n = p + 1 fp32 scores.  Output: the min(k, n) positions with
+// the largest scores, ties to the lower position, in ascending position
+// order, padded with -1 to k entries.
+//
+// Scores are compared through an order-preserving uint32 key (-0 folded onto
+// +0), so selection is exact integer work: a radix select with 8-bit digits
+// (LDS histograms) finds the k-th largest key K* and how many entries equal
+// to K* are taken; a stable, wave-ordered compaction then writes every entry
+// with key > K* and the first `need` entries with key == K*.
+//
+// One 1024-thread workgroup per row, three paths:
+//  A  n <= 16384: the whole row's keys sit in LDS; select there.
+//  B  longer rows: 8192 sampled scores (32 evenly spaced runs of 256) give
+//     a threshold tau expected to pass ~2.5k entries; one streaming pass
+//     keeps every entry with key >= tau in per-wave ordered LDS lists, and
+//     the exact select runs on those.  If fewer than k entries pass, or a
+//     list overflows, the row falls back to C.  The result never depends on
+//     the sample, only the cost does.
+//  C  exact radix select and compaction streaming the row from memory.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace lcsi {
+
+namespace {
+
+constexpr int NT = 1024;
+constexpr int NW = NT / 64;
+constexpr int NLDS = 16384;       // path A limit
+constexpr int CAPW = 512;         // candidate slots per wave (path B)
+constexpr int NSB = 32;           // sample runs
+constexpr int SBL = 256;          // run length
+constexpr int NSAMP = NSB * SBL;
+
+struct Shared {
+    union {
+        uint32_t keys[NLDS];                     // path A
+        uint32_t samp[NSAMP];                    // path B, before filtering
+        struct {
+            uint32_t key[NW * CAPW];
+            int32_t idx[NW * CAPW];
+        } cand;                                  // path B candidates
+    } u;
+    uint32_t hist[256];
+    int wcnt[NW];
+    int wgt[NW];
+    int wtie[NW];
+    uint32_t kth;
+    int rem;
+};
+
+// ---- element visitors: each thread calls f(key) for its share ------------
+
+struct LdsKeys {
+    const uint32_t *keys;
+    int n;
+    template <class F> __device__ void visit(F f) const
+    {
+        for (int i = threadIdx.x; i < n; i += NT) f(keys[i]);
+    }
+};
+
+struct Candidates {
+    const Shared *sh;
+    template <class F> __device__ void visit(F f) const
+    {
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int c = sh->wcnt[w];
+        for (int j = lane; j < c; j += 64) f(sh->u.cand.key[w * CAPW + j]);
+    }
+};
+
+struct GlobalRow {
+    const float *row;
+    int64_t n;
+    template <class F> __device__ void visit(F f) const
+    {
+        for (int64_t i = 4 * (int64_t)threadIdx.x; i < n; i += 4 * NT) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + i);
+            f(order_key(v.x));
+            if (i + 1 < n) f(order_key(v.y));
+            if (i + 2 < n) f(order_key(v.z));
+            if (i + 3 < n) f(order_key(v.w));
+        }
+    }
+};
+
+// Find the rank-th largest key (rank >= 1, at most the number of visited
+// keys).  On return sh.kth is that key and sh.rem the number of entries
+// equal to it that belong to the top `rank`.
+template <class Src>
+__device__ void radix_find(Shared &sh, const Src &src, int rank)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t prefix = 0, mask = 0;
+    int rem = rank;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) sh.hist[tid] = 0;
+        __syncthreads();
+        src.visit([&](uint32_t key) {
+            if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+        });
+        __syncthreads();
+        if (tid < 64) {
+            const uint32_t c0 = sh.hist[4 * lane], c1 = sh.hist[4 * lane + 1];
+            const uint32_t c2 = sh.hist[4 * lane + 2], c3 = sh.hist[4 * lane + 3];
+            const int tot = (int)(c0 + c1 + c2 + c3);
+            int suf = tot;  // inclusive suffix sum over lanes >= this one
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_down(suf, o);
+                if (lane + o < 64) suf += t;
+            }
+            const int above = suf - tot;
+            if (above < rem && rem <= suf) {
+                const uint32_t c[4] = {c0, c1, c2, c3};
+                int acc = above;
+                for (int e = 3; e >= 0; --e) {
+                    if (acc + (int)c[e] >= rem) {
+                        sh.kth = prefix | ((uint32_t)(4 * lane + e) << shift);
+                        sh.rem = rem - acc;
+                        break;
+                    }
+                    acc += (int)c[e];
+                }
+            }
+        }
+        __syncthreads();
+        prefix = sh.kth;
+        rem = sh.rem;
+        mask |= 0xFFu << shift;
+    }
+}
+
+// Ordered compaction over per-wave segments visited in ascending position
+// order.  Seg::get(w, j, key, pos) returns false past the end of segment w;
+// Seg::len(w) is an upper bound on its length (a multiple of 64 not needed).
+template <class Seg>
+__device__ void emit(Shared &sh, const Seg &seg, int32_t *out, int k)
+{
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const uint32_t kth = sh.kth;
+    const int need = sh.rem;
+    const int len = seg.len(w);
+    int gt = 0, tie = 0;
+    for (int j = lane; j < len; j += 64) {
+        uint32_t key;
+        int32_t pos;
+        if (seg.get(w, j, key, pos)) {
+            gt += key > kth;
+            tie += key == kth;
+        }
+    }
+    gt = wave_sum_int(gt);
+    tie = wave_sum_int(tie);
+    if (lane == 0) {
+        sh.wgt[w] = gt;
+        sh.wtie[w] = tie;
+    }
+    __syncthreads();
+    int tie_off = 0, out_off = 0;
+    for (int v = 0; v < w; ++v) {
+        const int take = min(max(need - tie_off, 0), sh.wtie[v]);
+        out_off += sh.wgt[v] + take;
+        tie_off += sh.wtie[v];
+    }
+    for (int j0 = 0; j0 < len; j0 += 64) {
+        uint32_t key = 0;
+        int32_t pos = -1;
+        const bool ok = seg.get(w, j0 + lane, key, pos);
+        const bool is_tie = ok && key == kth;
+        const uint64_t bt = ballot(is_tie);
+        const bool sel = ok && (key > kth || (is_tie && tie_off + lanes_below(bt) < need));
+        const uint64_t bs = ballot(sel);
+        const int slot = out_off + lanes_below(bs);
+        if (sel && slot < k) out[slot] = pos;
+        tie_off += __popcll(bt);
+        out_off += __popcll(bs);
+    }
+}
+
+struct LdsSeg {
+    const Shared *sh;
+    int n, seg;
+    __device__ int len(int w) const { return seg; }
+    __device__ bool get(int w, int j, uint32_t &key, int32_t &pos) const
+    {
+        const int i = w * seg + j;
+        if (j >= seg || i >= n) return false;
+        key = sh->u.keys[i];
+        pos = i;
+        return true;
+    }
+};
+
+struct CandSeg {
+    const Shared *sh;
+    __device__ int len(int w) const { return sh->wcnt[w]; }
+    __device__ bool get(int w, int j, uint32_t &key, int32_t &pos) const
+    {
+        if (j >= sh->wcnt[w]) return false;
+        key = sh->u.cand.key[w * CAPW + j];
+        pos = sh->u.cand.idx[w * CAPW + j];
+        return true;
+    }
+};
+
+struct GlobalSeg {
+    const float *row;
+    int64_t n, seg;
+    __device__ int len(int w) const { return (int)seg; }
+    __device__ bool get(int w, int j, uint32_t &key, int32_t &pos) const
+    {
+        const int64_t i = (int64_t)w * seg + j;
+        if (j >= seg || i >= n) return false;
+        key = order_key(row[i]);
+        pos = (int32_t)i;
+        return true;
+    }
+};
+
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
+{
+    __shared__ Shared sh;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int64_t n = a.q_pos0 + t + 1;
+    const int k = a.top_k;
+    const float *row = a.S + ((int64_t)b * a.T_q + t) * a.ld;
+    int32_t *out = a.idx + (int64_t)b * a.idx_sb + (int64_t)t * a.idx_st;
+
+    const int m = (int)min<int64_t>(n, k);
+    for (int j = m + tid; j < k; j += NT) out[j] = -1;
+    if (n <= k) {
+        for (int j = tid; j < m; j += NT) out[j] = j;
+        return;
+    }
+
+    if (n <= NLDS) {
+        // ---- path A: whole row in LDS
+        for (int i = 4 * tid; i < n; i += 4 * NT) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + i);
+            sh.u.keys[i] = order_key(v.x);
+            if (i + 1 < n) sh.u.keys[i + 1] = order_key(v.y);
+            if (i + 2 < n) sh.u.keys[i + 2] = order_key(v.z);
+            if (i + 3 < n) sh.u.keys[i + 3] = order_key(v.w);
+        }
+        __syncthreads();
+        radix_find(sh, LdsKeys{sh.u.keys, (int)n}, k);
+        const int seg = (int)(((n + NW - 1) / NW + 63) / 64 * 64);
+        emit(sh, LdsSeg{&sh, (int)n, seg}, out, k);
+        return;
+    }
+
+    // ---- path B: sampled threshold, one streaming pass, exact select on
+    // the candidates
+    for (int s = 2 * w; s < 2 * w + 2; ++s) {
+        const int64_t start = ((n - SBL) * s / (NSB - 1)) & ~(int64_t)3;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
+        uint32_t *d = sh.u.samp + s * SBL + 4 * lane;
+        d[0] = order_key(v.x);
+        d[1] = order_key(v.y);
+        d[2] = order_key(v.z);
+        d[3] = order_key(v.w);
+    }
+    __syncthreads();
+    int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
+    r = r < 1 ? 1 : (r > NSAMP ? NSAMP : r);
+    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r);
+    const uint32_t tau = sh.kth;
+    __syncthreads();  // every thread has read tau before the lists overwrite the samples
+
+    {
+        const int64_t seg = (n + NW * 256 - 1) / (NW * 256) * 256;
+        const int64_t lo = (int64_t)w * seg;
+        const int64_t hi = min<int64_t>(n, lo + seg);
+        int cnt = 0;
+        uint32_t *ck = sh.u.cand.key + w * CAPW;
+        int32_t *ci = sh.u.cand.idx + w * CAPW;
+        constexpr int U = 4;
+        for (int64_t base = lo; base < hi; base += U * 256) {
+            f32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + u * 256 + 4 * lane;
+                v[u] = i < hi ? *reinterpret_cast<const f32x4 *>(row + i) : f32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + u * 256 + 4 * lane;
+                const uint32_t k0 = order_key(v[u].x), k1 = order_key(v[u].y);
+                const uint32_t k2 = order_key(v[u].z), k3 = order_key(v[u].w);
+                const bool f0 = i < hi && k0 >= tau, f1 = i + 1 < hi && k1 >= tau;
+                const bool f2 = i + 2 < hi && k2 >= tau, f3 = i + 3 < hi && k3 >= tau;
+                const int c = (int)f0 + (int)f1 + (int)f2 + (int)f3;
+                if (ballot(c > 0) == 0) continue;
+                const uint64_t b0 = ballot(c & 1), b1 = ballot(c & 2), b2 = ballot(c & 4);
+                int p = cnt + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
+                if (f0) { if (p < CAPW) { ck[p] = k0; ci[p] = (int32_t)i; } ++p; }
+                if (f1) { if (p < CAPW) { ck[p] = k1; ci[p] = (int32_t)(i + 1); } ++p; }
+                if (f2) { if (p < CAPW) { ck[p] = k2; ci[p] = (int32_t)(i + 2); } ++p; }
+                if (f3) { if (p < CAPW) { ck[p] = k3; ci[p] = (int32_t)(i + 3); } ++p; }
+                cnt += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+            }
+        }
+        if (lane == 0) sh.wcnt[w] = cnt;
+    }
+    __syncthreads();
+    int total = 0;
+    bool overflow = false;
+    for (int v = 0; v < NW; ++v) {
+        total += sh.wcnt[v];
+        overflow |= sh.wcnt[v] > CAPW;
+    }
+    if (!overflow && total >= k) {
+        radix_find(sh, Candidates{&sh}, k);
+        emit(sh, CandSeg{&sh}, out, k);
+        return;
+    }
+
+    // ---- path C: exact, streaming the row from memory
+    __syncthreads();
+    radix_find(sh, GlobalRow{row, n}, k);
+    const int64_t seg = ((n + NW - 1) / NW + 63) / 64 * 64;
+    emit(sh, GlobalSeg{row, n, seg}, out, k);
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs &a, hipStream_t st)
+{
+    dim3 grid(a.T_q, a.B);
+    hipLaunchKernelGGL(select_kernel, grid, dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace lcsi

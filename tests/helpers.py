@@ -1,0 +1,62 @@
+"""Shared helpers for the GPU parity tests: host copies in the oracle's
+formats and the tolerance checks (scores within 1e-2 relative with a floor
+of 1e-3 of the row's largest magnitude; index sets equal except near-ties
+within that tolerance of the k-th value; attention max-abs <= 2e-2)."""
+import sys
+
+import numpy as np
+import torch
+
+SCORE_RTOL = 1e-2
+FLOOR = 1e-3
+ATTN_ATOL = 2e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 bit patterns on the host."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bytes_u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def check_scores(g_row: np.ndarray, r_row: np.ndarray, what=""):
+    """g_row, r_row: float32 scores of one row over its causal keys."""
+    r = r_row.astype(np.float64)
+    g = g_row.astype(np.float64)
+    floor = FLOOR * np.max(np.abs(r)) if r.size else 0.0
+    tol = SCORE_RTOL * np.maximum(np.abs(r), floor)
+    bad = np.abs(g - r) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} scores off, worst at {np.argmax(np.abs(g - r) - tol)}"
+
+
+def check_index_sets(g_idx: np.ndarray, r_idx: np.ndarray, r_row: np.ndarray, k: int, what=""):
+    """Equal sets except entries whose oracle score is within tolerance of the
+    oracle's k-th largest value (legitimate near-tie swaps)."""
+    g = set(int(x) for x in g_idx if x >= 0)
+    r = set(int(x) for x in r_idx if x >= 0)
+    assert len(g) == len(r), f"{what}: set sizes {len(g)} vs {len(r)}"
+    assert list(g_idx[:len(g)]) == sorted(g), f"{what}: not ascending"
+    assert np.all(g_idx[len(g):] == -1), f"{what}: bad padding"
+    diff = g ^ r
+    if not diff:
+        return 0
+    rr = r_row.astype(np.float64)
+    n = len(rr)
+    vk = np.sort(rr)[::-1][min(k, n) - 1]
+    floor = FLOOR * np.max(np.abs(rr))
+    tol = SCORE_RTOL * max(abs(vk), floor)
+    for s in diff:
+        assert abs(rr[s] - vk) <= tol, f"{what}: index {s} score {rr[s]} vs k-th {vk}"
+    return len(diff)

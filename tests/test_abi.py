@@ -1,0 +1,253 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/lcsi.h declares, and rejects every bad argument with
+its status code before anything is launched.  Pointers here are fake but
+aligned addresses: validation only looks at NULL-ness and alignment, and
+every call below either fails validation or runs in query mode, so nothing
+is ever dereferenced or launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_sparse_idx_amd import lcsi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcsi.h")
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}()]*(?:\([^)]*\)[^;{}()]*)*\)\s*;", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("idx_score_topk", "sparse_attn", "run_layer_group"):
+        assert n in names
+    assert set(names) == set(lcsi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", lcsi._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lcsi.lib, name)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lcsi.strerror(code)
+    assert lcsi.strerror(-99) == "unknown status"
+
+
+def test_score_ld():
+    assert lcsi.score_ld(1) == 64
+    assert lcsi.score_ld(64) == 64
+    assert lcsi.score_ld(200000) == 200000
+    assert lcsi.score_ld(131073) == 131136
+
+
+# ---------------------------------------------------------------- indexer
+
+def good_indexer(**over):
+    d = lcsi.Indexer()
+    d.B, d.T_q, d.T_kv, d.H_I, d.D_I, d.top_k = 2, 16, 100, 64, 128, 8
+    d.key_dtype = lcsi.LCSI_KEY_BF16
+    d.q_pos0 = 84
+    d.q, d.q_sb, d.q_st, d.q_sh = FAKE, 16 * 64 * 128, 64 * 128, 128
+    d.k, d.k_sb, d.k_st = FAKE, 100 * 128, 128
+    d.w, d.w_sb, d.w_st = FAKE, 16 * 64, 64
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def call_idx(d, idx=FAKE, ws=None, nbytes=None, flags=0, sb=16 * 8, st=8):
+    n = ctypes.c_size_t(nbytes if nbytes is not None else 0)
+    ref = ctypes.byref(n) if nbytes is not None or ws is None else None
+    rc = lcsi.lib.idx_score_topk(ctypes.byref(d), ctypes.c_void_p(idx), sb, st,
+                                 ctypes.c_void_p(ws) if ws else None, ref, flags, None)
+    return rc, n.value
+
+
+def test_indexer_query_mode_returns_workspace_size():
+    rc, n = call_idx(good_indexer())
+    assert rc == 0
+    assert n == 2 * 16 * lcsi.score_ld(100) * 4
+    rc, n = call_idx(good_indexer(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE, ks_sb=100,
+                                  k_sb=100 * 128, k_st=128))
+    assert rc == 0 and n > 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", 0, lcsi.LCSI_EINVAL),
+    ("T_q", 0, lcsi.LCSI_EINVAL),
+    ("T_kv", 0, lcsi.LCSI_EINVAL),
+    ("q_pos0", -1, lcsi.LCSI_EINVAL),
+    ("q_pos0", 85, lcsi.LCSI_EINVAL),          # q_pos0 + T_q > T_kv
+    ("top_k", 0, lcsi.LCSI_EINVAL),
+    ("top_k", 2049, lcsi.LCSI_EUNSUPPORTED),
+    ("H_I", 0, lcsi.LCSI_EINVAL),
+    ("H_I", 12, lcsi.LCSI_EUNSUPPORTED),
+    ("H_I", 128, lcsi.LCSI_EUNSUPPORTED),
+    ("D_I", 96, lcsi.LCSI_EUNSUPPORTED),
+    ("key_dtype", 7, lcsi.LCSI_EINVAL),
+    ("q", 0, lcsi.LCSI_EINVAL),
+    ("k", 0, lcsi.LCSI_EINVAL),
+    ("w", 0, lcsi.LCSI_EINVAL),
+    ("q", FAKE + 8, lcsi.LCSI_EALIGN),
+    ("k", FAKE + 2, lcsi.LCSI_EALIGN),
+    ("w", FAKE + 4, lcsi.LCSI_EALIGN),
+    ("q_sh", 132, lcsi.LCSI_EALIGN),
+    ("k_st", 130, lcsi.LCSI_EALIGN),
+    ("w_st", 66, lcsi.LCSI_EALIGN),
+    ("q_st", -8, lcsi.LCSI_EINVAL),
+])
+def test_indexer_rejects_bad_fields(field, value, code):
+    rc, _ = call_idx(good_indexer(**{field: value}))
+    assert rc == code
+
+
+def test_indexer_fp8_needs_scale_and_16_byte_rows():
+    d = good_indexer(key_dtype=lcsi.LCSI_KEY_FP8_E4M3)
+    assert call_idx(d)[0] == lcsi.LCSI_EINVAL                 # no k_scale
+    d = good_indexer(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE + 2, ks_sb=100)
+    assert call_idx(d)[0] == lcsi.LCSI_EALIGN
+    d = good_indexer(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE, ks_sb=100, k_st=136)
+    assert call_idx(d)[0] == lcsi.LCSI_EALIGN                 # 136 B rows
+
+
+def test_indexer_output_and_flags():
+    need = call_idx(good_indexer())[1]
+    # output checks apply when a workspace is given (not in query mode)
+    assert call_idx(good_indexer(), idx=0, ws=FAKE, nbytes=need)[0] == lcsi.LCSI_EINVAL
+    assert call_idx(good_indexer(), idx=FAKE + 2, ws=FAKE, nbytes=need)[0] == lcsi.LCSI_EALIGN
+    assert call_idx(good_indexer(), st=-1, ws=FAKE, nbytes=need)[0] == lcsi.LCSI_EINVAL
+    assert call_idx(good_indexer(), flags=3)[0] == lcsi.LCSI_EINVAL
+    assert call_idx(good_indexer(), flags=8)[0] == lcsi.LCSI_EINVAL
+    # query mode needs only the descriptor
+    assert call_idx(good_indexer(), idx=0) == (0, need)
+    # scores-only needs no index output
+    assert call_idx(good_indexer(), idx=0, flags=lcsi.LCSI_SCORES_ONLY)[0] == 0
+    # preset mode reads only B, T_q, T_kv, q_pos0, top_k
+    d = lcsi.preset_desc(2, 16, 100, 84, 8)
+    rc, n = call_idx(d, flags=lcsi.LCSI_SCORES_PRESET)
+    assert rc == 0 and n == 2 * 16 * 128 * 4
+
+
+def test_indexer_workspace_rules():
+    need = call_idx(good_indexer())[1]
+    # no workspace and no size pointer: a workspace is always required
+    rc = lcsi.lib.idx_score_topk(ctypes.byref(good_indexer()), ctypes.c_void_p(FAKE), 128, 8,
+                                 None, None, 0, None)
+    assert rc == lcsi.LCSI_EWORKSPACE
+    # a workspace without its capacity
+    rc = lcsi.lib.idx_score_topk(ctypes.byref(good_indexer()), ctypes.c_void_p(FAKE), 128, 8,
+                                 ctypes.c_void_p(FAKE), None, 0, None)
+    assert rc == lcsi.LCSI_EINVAL
+    assert call_idx(good_indexer(), ws=FAKE, nbytes=need - 1)[0] == lcsi.LCSI_EWORKSPACE
+    assert call_idx(good_indexer(), ws=FAKE + 128, nbytes=need)[0] == lcsi.LCSI_EALIGN
+
+
+# -------------------------------------------------------------- attention
+
+def good_attn(**over):
+    d = lcsi.Attn()
+    d.B, d.T_q, d.T_kv, d.H_q, d.D_qk, d.D_v, d.top_k = 2, 16, 100, 32, 576, 512, 8
+    d.sm_scale = 0.04
+    d.q_pos0 = 84
+    d.q, d.q_sb, d.q_st, d.q_sh = FAKE, 16 * 32 * 576, 32 * 576, 576
+    d.k, d.k_sb, d.k_st = FAKE, 100 * 576, 576
+    d.v, d.v_sb, d.v_st = FAKE, 100 * 576, 576
+    d.out, d.o_sb, d.o_st, d.o_sh = FAKE, 16 * 32 * 512, 32 * 512, 512
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def call_attn(d, idx=FAKE, query=True):
+    n = ctypes.c_size_t(0)
+    return lcsi.lib.sparse_attn(ctypes.byref(d), ctypes.c_void_p(idx), 128, 8, None,
+                                ctypes.byref(n) if query else None, None), n.value
+
+
+def test_attn_query_mode():
+    rc, n = call_attn(good_attn(top_k=2048))
+    assert rc == 0 and n > 0            # 32 rows, long lists: split partials are needed
+    rc, n = call_attn(good_attn(B=1, T_q=1024, q_pos0=0, T_kv=1024))
+    assert rc == 0 and n == 0           # enough rows: no workspace
+    # a workspace-free call is refused when partials are needed
+    assert call_attn(good_attn(top_k=2048), query=False)[0] == lcsi.LCSI_EWORKSPACE
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", 0, lcsi.LCSI_EINVAL),
+    ("q_pos0", 90, lcsi.LCSI_EINVAL),
+    ("top_k", 0, lcsi.LCSI_EINVAL),
+    ("top_k", 4096, lcsi.LCSI_EUNSUPPORTED),
+    ("H_q", 0, lcsi.LCSI_EINVAL),
+    ("H_q", 65, lcsi.LCSI_EUNSUPPORTED),
+    ("D_qk", 192, lcsi.LCSI_EUNSUPPORTED),
+    ("D_v", 128, lcsi.LCSI_EUNSUPPORTED),
+    ("sm_scale", float("inf"), lcsi.LCSI_EINVAL),
+    ("sm_scale", float("nan"), lcsi.LCSI_EINVAL),
+    ("q", 0, lcsi.LCSI_EINVAL),
+    ("out", 0, lcsi.LCSI_EINVAL),
+    ("v", FAKE + 2, lcsi.LCSI_EALIGN),
+    ("k_st", 580, lcsi.LCSI_EALIGN),
+    ("o_sh", 516, lcsi.LCSI_EALIGN),
+])
+def test_attn_rejects_bad_fields(field, value, code):
+    assert call_attn(good_attn(**{field: value}))[0] == code
+
+
+def test_attn_rejects_bad_index_pointer():
+    # outside query mode (no workspace needed at top_k = 8): index checks apply
+    assert call_attn(good_attn(), idx=0, query=False)[0] == lcsi.LCSI_EINVAL
+    assert call_attn(good_attn(), idx=FAKE + 1, query=False)[0] == lcsi.LCSI_EALIGN
+    # query mode needs only the descriptor
+    assert call_attn(good_attn(), idx=0)[0] == 0
+
+
+# ------------------------------------------------------------ layer group
+
+def call_group(pattern, n_idx=None, idx_over=None, attn_over=None, n_slots=1, cache=FAKE, query=True):
+    L = len(pattern)
+    nf = sum(pattern) if n_idx is None else n_idx
+    pat = (ctypes.c_uint8 * L)(*pattern)
+    ia = (lcsi.Indexer * max(nf, 1))(*[good_indexer(**(idx_over or {})) for _ in range(max(nf, 1))])
+    aa = (lcsi.Attn * L)(*[good_attn(**(attn_over or {})) for _ in range(L)])
+    n = ctypes.c_size_t(0)
+    if query:
+        rc = lcsi.lib.run_layer_group(L, pat, ia, nf, aa, ctypes.c_void_p(cache), n_slots, 0, 128, 8,
+                                      None, ctypes.byref(n), None, None)
+    else:  # a workspace that is too small: fails before any launch
+        n.value = 1
+        rc = lcsi.lib.run_layer_group(L, pat, ia, nf, aa, ctypes.c_void_p(cache), n_slots, 0, 128, 8,
+                                      ctypes.c_void_p(FAKE), ctypes.byref(n), None, None)
+    return rc, n.value
+
+
+def test_layer_group_query_and_pattern_errors():
+    rc, n = call_group([1, 0, 0, 0])
+    assert rc == 0 and n >= 2 * 16 * 128 * 4
+    assert call_group([0, 1, 0, 0])[0] == lcsi.LCSI_EPATTERN     # leading S
+    assert call_group([1, 0, 1, 0], n_idx=1)[0] == lcsi.LCSI_EPATTERN
+    assert call_group([1, 0, 0, 0], n_idx=2)[0] == lcsi.LCSI_EPATTERN
+    assert call_group([1, 0], n_slots=0)[0] == lcsi.LCSI_EINVAL
+    assert call_group([1, 0], cache=0)[0] == 0                       # query: descriptors only
+    assert call_group([1, 0], cache=0, query=False)[0] == lcsi.LCSI_EINVAL
+    assert call_group([1, 0], cache=FAKE + 2, query=False)[0] == lcsi.LCSI_EALIGN
+    assert call_group([1, 0], query=False)[0] == lcsi.LCSI_EWORKSPACE
+    # descriptors of one group must agree on rows and top_k
+    assert call_group([1, 0], attn_over={"top_k": 16})[0] == lcsi.LCSI_EINVAL
+    assert call_group([1, 0], idx_over={"H_I": 48})[0] == lcsi.LCSI_EUNSUPPORTED
+    assert call_group([1, 0], attn_over={"D_qk": 64})[0] == lcsi.LCSI_EUNSUPPORTED

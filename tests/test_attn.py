@@ -1,0 +1,134 @@
+"""GPU sparse attention against the oracle on the same index sets.
+
+Max-abs error <= 2e-2 in bf16 output units; a single index returns that V
+row exactly; appended unusable indices (negative, beyond the row's position,
+beyond T_kv) change nothing, bit for bit; permuting an index row changes the
+result only within rounding.  Covers the separate-K/V tiny shape (Dqk = Dv =
+128, 8 heads) and the MLA-style shared 576-wide row with V = its first 512
+columns at 16, 32 and 64 heads, both with one workgroup per row and with the
+split + merge used when few rows are present (decode)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import ATTN_ATOL, bf16_to_f64, bits, log
+from long_context_sparse_idx_amd import lcsi
+
+pytestmark = pytest.mark.gpu
+
+
+def make(B, T_kv, H, Dqk, Dv, shared, T_q, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, T_q, H, Dqk, generator=g).to(torch.bfloat16)
+    if shared:
+        kv = torch.randn(B, T_kv, Dqk, generator=g).to(torch.bfloat16)
+        return q, kv, kv[..., :Dv]
+    k = torch.randn(B, T_kv, Dqk, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, T_kv, Dv, generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
+def random_sets(B, T_q, q_pos0, k, rng):
+    idx = np.full((B, T_q, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T_q):
+            n = q_pos0 + t + 1
+            m = min(k, n)
+            idx[b, t, :m] = np.sort(rng.choice(n, m, replace=False))
+    return idx
+
+
+def gpu_attn(q, k, v, idx, q_pos0, tau):
+    B, T_q, H, _ = q.shape
+    Dv = v.shape[-1]
+    out = torch.full((B, T_q, H, Dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d = lcsi.attn_desc(q, k, v, out, idx.shape[-1], q_pos0, tau)
+    lcsi.sparse_attn(d, idx)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_attn(q, k, v, idx, tau, shared):
+    outs = []
+    for b in range(q.shape[0]):
+        K = bits(k[b])
+        V = (K, v.shape[-1]) if shared else bits(v[b])
+        outs.append(oracle.attn(bits(q[b]), K, V, idx[b], tau))
+    return np.stack(outs)
+
+
+CASES = [
+    # B, T_q, T_kv, q_pos0, H, Dqk, Dv, shared, k
+    (1, 200, 300, 100, 8, 128, 128, False, 64),     # tiny shape
+    (1, 96, 3000, 2904, 32, 576, 512, True, 2048),  # prefill-like, 32 heads
+    (1, 64, 2500, 2436, 64, 576, 512, True, 512),
+    (1, 40, 900, 860, 16, 576, 512, True, 100),     # ragged last tile
+    (3, 1, 5000, 4999, 64, 576, 512, True, 2048),   # decode: split + merge
+    (2, 2, 3000, 2998, 32, 576, 512, True, 1000),
+    (2, 1, 700, 699, 8, 128, 128, False, 333),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_attn_matches_oracle(case):
+    B, T_q, T_kv, q_pos0, H, Dqk, Dv, shared, k = case
+    log(f"[attn] case={case}")
+    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    q, kk, v = make(B, T_kv, H, Dqk, Dv, shared, T_q, seed=abs(hash(case)) % 1000)
+    idx = random_sets(B, T_q, q_pos0, k, rng)
+    tau = Dqk ** -0.5
+    dq, dk = q.cuda(), kk.cuda()
+    dv = dk[..., :Dv] if shared else v.cuda()
+    g = gpu_attn(dq, dk, dv, torch.from_numpy(idx).cuda(), q_pos0, tau)
+    gb = bits(g)
+    r = oracle_attn(q, kk, v, idx, tau, shared)
+    err = np.abs(bf16_to_f64(gb) - bf16_to_f64(r))
+    log(f"  max abs err {err.max():.3e}")
+    assert np.isfinite(bf16_to_f64(gb)).all()
+    assert err.max() <= ATTN_ATOL
+
+
+def test_attn_single_index_is_exact_row():
+    B, T_q, T_kv, H, Dqk, Dv = 1, 50, 600, 64, 576, 512
+    q, kv, _ = make(B, T_kv, H, Dqk, Dv, True, T_q, seed=3)
+    rng = np.random.default_rng(3)
+    q_pos0 = T_kv - T_q
+    idx = np.array([[[rng.integers(0, q_pos0 + t + 1)] for t in range(T_q)]], np.int32)
+    dkv = kv.cuda()
+    g = gpu_attn(q.cuda(), dkv, dkv[..., :Dv], torch.from_numpy(idx).cuda(), q_pos0, 0.05)
+    gb = bits(g)[0]
+    V = bits(kv[0])[:, :Dv]
+    for t in range(T_q):
+        for h in range(H):
+            assert np.array_equal(gb[t, h], V[idx[0, t, 0]])
+
+
+def test_attn_skips_unusable_indices_and_is_order_insensitive():
+    B, T_q, T_kv, H, Dqk, Dv, k = 2, 20, 1500, 32, 576, 512, 256
+    q_pos0 = 1000
+    q, kv, _ = make(B, T_kv, H, Dqk, Dv, True, T_q, seed=4)
+    rng = np.random.default_rng(4)
+    idx = random_sets(B, T_q, q_pos0, k, rng)
+    dq, dkv = q.cuda(), kv.cuda()
+    base = bits(gpu_attn(dq, dkv, dkv[..., :Dv], torch.from_numpy(idx).cuda(), q_pos0, 0.04))
+    junk = np.empty((B, T_q, 64), np.int32)
+    for b in range(B):
+        for t in range(T_q):
+            p = q_pos0 + t
+            junk[b, t] = rng.choice(np.array([-1, -5, p + 1, p + 300, T_kv, T_kv + 10 ** 6], np.int64), 64)
+    idx2 = np.concatenate([idx, junk], axis=2)
+    out2 = bits(gpu_attn(dq, dkv, dkv[..., :Dv], torch.from_numpy(idx2).cuda(), q_pos0, 0.04))
+    assert np.array_equal(base, out2)
+    perm = idx[:, :, rng.permutation(k)]
+    out3 = bits(gpu_attn(dq, dkv, dkv[..., :Dv], torch.from_numpy(np.ascontiguousarray(perm)).cuda(),
+                         q_pos0, 0.04))
+    assert np.abs(bf16_to_f64(out3) - bf16_to_f64(base)).max() <= ATTN_ATOL
+
+
+def test_attn_no_usable_index_gives_zeros():
+    B, T_q, T_kv, H, Dqk, Dv, k = 1, 4, 300, 16, 128, 128, 32
+    q, kk, v = make(B, T_kv, H, Dqk, Dv, False, T_q, seed=6)
+    idx = torch.full((B, T_q, k), -1, dtype=torch.int32)
+    g = gpu_attn(q.cuda(), kk.cuda(), v.cuda(), idx.cuda(), T_kv - T_q, 0.1)
+    assert torch.equal(g.float().cpu(), torch.zeros(B, T_q, H, Dv))

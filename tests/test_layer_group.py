@@ -1,0 +1,182 @@
+"""run_layer_group: the F/S loop.
+
+All-F equals a per-layer loop of the two calls, byte for byte; an S layer's
+index set is byte-identical to its F layer's; an S layer's output equals
+sparse_attn with its own inputs on the F layer's indices; the whole group
+matches the oracle's layer loop (indices exact here, where no near-ties
+occur at these sizes, else within the near-tie rule; outputs within 2e-2).
+Patterns: FSSS (tiny workload), FSSSFSSS with one shared slot, and F at
+{0,3,4,8} of 12 with one slot per F layer.  Per-layer events are recorded."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import ATTN_ATOL, bf16_to_f64, bits, check_index_sets, log
+from long_context_sparse_idx_amd import inputs, lcsi
+
+pytestmark = pytest.mark.gpu
+
+
+def build(wl, device="cpu"):
+    f_in, a_in = [], []
+    for l, is_f in enumerate(wl.pattern):
+        if is_f:
+            f_in.append(inputs.indexer_inputs(wl, l, device))
+        a_in.append(inputs.attn_inputs(wl, l, device))
+    return f_in, a_in
+
+
+def descs(wl, f_dev, a_dev, outs):
+    tau = inputs.sm_scale(wl)
+    ids = [lcsi.indexer_desc(x["q"], x["k"], x["w"], wl.top_k, wl.q_pos0, k_scale=x["k_scale"])
+           for x in f_dev]
+    ads = [lcsi.attn_desc(x["q"], x["k"], x["v"], o, wl.top_k, wl.q_pos0, tau) for x, o in zip(a_dev, outs)]
+    return ids, ads
+
+
+def to_dev(d):
+    return {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+
+
+def attn_dev(x):
+    y = {"q": x["q"].cuda(), "k": x["k"].cuda()}
+    y["v"] = y["k"][..., :x["v"].shape[-1]] if x["v"].data_ptr() == x["k"].data_ptr() else x["v"].cuda()
+    return y
+
+
+def run_group(wl, pattern, f_dev, a_dev, n_slots, with_events=False):
+    L = len(pattern)
+    B, T_q, k = wl.B, wl.n_q, wl.top_k
+    outs = [torch.empty((B, T_q, wl.H_q, wl.D_v), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    ids, ads = descs(wl, f_dev, a_dev, outs)
+    cache = torch.full((n_slots, B, T_q, k), -9, dtype=torch.int32, device="cuda")
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] if with_events else None
+    lcsi.run_layer_group(pattern, ids, ads, cache, n_slots, B * T_q * k, T_q * k, k, events=events)
+    torch.cuda.synchronize()
+    return outs, cache, events
+
+
+def small(name, **over):
+    return dataclasses.replace(inputs.WORKLOADS[name], **over)
+
+
+def test_tiny_fsss_against_oracle_and_invariants():
+    wl = inputs.WORKLOADS["tiny"]
+    log("[group] tiny FSSS")
+    f_in, a_in = build(wl)
+    f_dev = [to_dev(x) for x in f_in]
+    a_dev = [attn_dev(x) for x in a_in]
+    outs, cache, events = run_group(wl, wl.pattern, f_dev, a_dev, n_slots=1, with_events=True)
+    for e in events:
+        assert e.query()
+    assert all(events[i].elapsed_time(events[i + 1]) >= 0 for i in range(len(events) - 1))
+    # S layers: identical to sparse_attn on the F layer's set
+    idx_f = cache[0]
+    for l in range(4):
+        out = torch.empty_like(outs[l])
+        x = a_dev[l]
+        d = lcsi.attn_desc(x["q"], x["k"], x["v"], out, wl.top_k, wl.q_pos0, inputs.sm_scale(wl))
+        lcsi.sparse_attn(d, idx_f)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), outs[l].view(torch.int16))
+    # against the oracle's layer loop on a sample of rows
+    rows = sorted({0, 1, 63, 64, 65, 500, 1024, 2046, 2047})
+    pos = np.array(rows, np.int64)
+    f_layers = [dict(q=bits(x["q"][0, rows]), w=x["w"][0, rows].numpy(), keys=bits(x["k"][0]))
+                for x in f_in]
+    a_layers = [dict(q=bits(x["q"][0, rows]), K=bits(x["k"][0]), V=bits(x["v"][0]),
+                     tau=inputs.sm_scale(wl)) for x in a_in]
+    r_idx, r_out = oracle.layer_group(wl.pattern, f_layers, a_layers, pos, wl.top_k)
+    g_idx = cache[0, 0].cpu().numpy()
+    rS, _ = oracle.score_select(f_layers[0]["q"], f_layers[0]["w"], f_layers[0]["keys"], pos, wl.top_k)
+    for i, t in enumerate(rows):
+        check_index_sets(g_idx[t], r_idx[0][i], rS[i, :t + 1], wl.top_k, f"row {t}")
+    for l in range(4):
+        # evaluate the oracle on the GPU's validated index set for the output check
+        o = oracle.attn(a_layers[l]["q"], a_layers[l]["K"], a_layers[l]["V"], g_idx[rows], a_layers[l]["tau"])
+        err = np.abs(bf16_to_f64(bits(outs[l][0, rows])) - bf16_to_f64(o)).max()
+        assert err <= ATTN_ATOL, (l, err)
+
+
+def test_all_f_equals_per_layer_calls_and_s_reuse():
+    wl = small("prefill32k", n_q=256, q_pos0=3840, T_kv=4096, T_q=256, top_k=512)
+    log("[group] all-F vs per-layer, FSSS reuse")
+    f_in = [inputs.indexer_inputs(wl, l, "cpu") for l in range(4)]
+    a_in = [inputs.attn_inputs(wl, l, "cpu") for l in range(4)]
+    f_dev = [to_dev(x) for x in f_in]
+    a_dev = [attn_dev(x) for x in a_in]
+    outs_f, cache_f, _ = run_group(wl, (1, 1, 1, 1), f_dev, a_dev, n_slots=4)
+    # per-layer DSA loop
+    for l in range(4):
+        x = f_dev[l]
+        d = lcsi.indexer_desc(x["q"], x["k"], x["w"], wl.top_k, wl.q_pos0)
+        ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4, device="cuda")
+        idx = torch.empty((1, wl.n_q, wl.top_k), dtype=torch.int32, device="cuda")
+        lcsi.idx_score_topk(d, idx, ws)
+        out = torch.empty_like(outs_f[l])
+        y = a_dev[l]
+        lcsi.sparse_attn(lcsi.attn_desc(y["q"], y["k"], y["v"], out, wl.top_k, wl.q_pos0,
+                                        inputs.sm_scale(wl)), idx)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, cache_f[l])
+        assert torch.equal(out.view(torch.int16), outs_f[l].view(torch.int16))
+    # FSSS: every layer sees layer 0's set; outputs of S layers differ from all-F
+    outs_s, cache_s, _ = run_group(wl, (1, 0, 0, 0), f_dev[:1], a_dev, n_slots=1)
+    assert torch.equal(cache_s[0], cache_f[0])
+    assert torch.equal(outs_s[0].view(torch.int16), outs_f[0].view(torch.int16))
+    # adjacent-layer overlap of the synthetic generator (noise 0.3): report it
+    a = cache_f[0].cpu().numpy()[0]
+    ov = []
+    for l in range(1, 4):
+        b = cache_f[l].cpu().numpy()[0]
+        ov.append(np.mean([len(np.intersect1d(a[t], b[t])) / wl.top_k for t in range(0, wl.n_q, 16)]))
+    log(f"  overlap with layer 0: {[round(x, 3) for x in ov]}")
+
+
+@pytest.mark.parametrize("name,n_slots", [("decode131k", 1), ("decode1m", 4)])
+def test_decode_patterns(name, n_slots):
+    """Decode-shaped groups (few rows, split kernels) at reduced context:
+    FSSSFSSS with a single shared slot, and F at {0,3,4,8} of 12 with fp8 keys
+    and one slot per F layer."""
+    base = inputs.WORKLOADS[name]
+    wl = dataclasses.replace(base, B=2, q_pos0=6000, T_kv=6001)
+    log(f"[group] {name} reduced, slots={n_slots}")
+    f_in, a_in = build(wl)
+    f_dev = [to_dev(x) for x in f_in]
+    a_dev = [attn_dev(x) for x in a_in]
+    outs, cache, _ = run_group(wl, wl.pattern, f_dev, a_dev, n_slots=n_slots)
+    pos = np.array([wl.q_pos0], np.int64)
+    f_pos = [l for l, f in enumerate(wl.pattern) if f]
+    for b in range(wl.B):
+        cur = None
+        fi = 0
+        for l, is_f in enumerate(wl.pattern):
+            if is_f:
+                x = f_in[fi]
+                keys = x["k"][b].numpy() if wl.key_fp8 else bits(x["k"][b])
+                rS, ridx = oracle.score_select(bits(x["q"][b]), x["w"][b].numpy(), keys, pos, wl.top_k,
+                                               k_scale=x["k_scale"][b].numpy() if wl.key_fp8 else None)
+                slot = fi % n_slots
+                cur = cache[slot, b].cpu().numpy()
+                if n_slots > 1 or fi == len(f_pos) - 1:
+                    check_index_sets(cur[0], ridx[0], rS[0, :wl.q_pos0 + 1], wl.top_k, f"b={b} l={l}")
+                fi += 1
+            y = a_in[l]
+            K = bits(y["k"][b])
+            o = oracle.attn(bits(y["q"][b]), K, (K, wl.D_v), cur, inputs.sm_scale(wl))
+            if n_slots > 1 or l >= f_pos[-1]:
+                err = np.abs(bf16_to_f64(bits(outs[l][b])) - bf16_to_f64(o)).max()
+                assert err <= ATTN_ATOL, (b, l, err)
+
+
+def test_leading_s_layer_is_rejected():
+    wl = inputs.WORKLOADS["tiny"]
+    f_in, a_in = build(wl)
+    f_dev = [to_dev(x) for x in f_in]
+    a_dev = [attn_dev(x) for x in a_in]
+    with pytest.raises(lcsi.LcsiError) as e:
+        run_group(wl, (0, 1, 0, 0), f_dev, a_dev, n_slots=1)
+    assert e.value.code == lcsi.LCSI_EPATTERN

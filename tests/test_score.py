@@ -1,0 +1,141 @@
+"""GPU indexer scores and end-to-end indices against the oracle.
+
+Integer-exact mode (q, k integers in [-8, 8], w powers of two) makes every
+score an exactly representable fp32 value whatever the summation order, so
+GPU scores must equal the oracle's bit for bit and the indices must match
+exactly.  Gaussian inputs are checked at the 1e-2 score tolerance and the
+near-tie rule for index sets.  Both score kernels (the LDS-staged prefill
+kernel and the split-key kernel used for few rows) and both key dtypes
+(bf16, fp8 e4m3 + scale) are covered, with ragged tails."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_idx_amd import inputs, lcsi
+from helpers import bits, bytes_u8, check_index_sets, check_scores, log
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None):
+    """Returns (scores [B, T_q, ld] float32 host, idx [B, T_q, k] host)."""
+    B, T_q = q.shape[:2]
+    T_kv = k.shape[1]
+    d = lcsi.indexer_desc(q, k, w, top_k, q_pos0, k_scale=k_scale)
+    ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4, dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, T_q, top_k), dtype=torch.int32, device="cuda")
+    lcsi.idx_score_topk(d, idx, ws)
+    torch.cuda.synchronize()
+    return ws.view(B, T_q, lcsi.score_ld(T_kv)).cpu().numpy(), idx.cpu().numpy()
+
+
+def int_inputs(B, T_q, T_kv, H, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randint(-8, 9, (B, T_q, H, D), generator=g).to(torch.bfloat16)
+    k = torch.randint(-8, 9, (B, T_kv, D), generator=g).to(torch.float32)
+    w = (2.0 ** torch.randint(-3, 1, (B, T_q, H), generator=g)).to(torch.float32)
+    return q, k, w
+
+
+SHAPES = [
+    # B, T_q, T_kv, q_pos0, H, D, k         kernel the library picks
+    (1, 300, 300, 0, 4, 64, 64),           # prefill (LDS-staged), causal from 0
+    (1, 2048, 4100, 2052, 64, 128, 256),   # prefill, offset chunk, ragged key tail
+    (1, 130, 1000, 870, 16, 128, 100),     # prefill, H=16
+    (3, 1, 9001, 9000, 64, 128, 2048),     # decode rows: split-key
+    (2, 3, 8192, 8189, 8, 64, 512),        # few rows: split-key, H=8, D=64
+    (1, 2, 6000, 5998, 32, 128, 128),      # few rows: split-key, H=32
+]
+
+
+def check_rows(T_q):
+    """Rows checked against the oracle: both ends and a spread in between."""
+    r = {0, 1, T_q - 2, T_q - 1} | set(np.linspace(0, T_q - 1, 10).astype(int).tolist())
+    return sorted(x for x in r if 0 <= x < T_q)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_score_integer_exact(shape, fp8):
+    B, T_q, T_kv, q_pos0, H, D, k = shape
+    log(f"[score-int] shape={shape} fp8={fp8}")
+    q, kf, w = int_inputs(B, T_q, T_kv, H, D, seed=hash(shape) % 1000 + fp8)
+    if fp8:
+        kk = kf.to(torch.float8_e4m3fn)           # integers |x| <= 8 are exact in e4m3
+        scale = (2.0 ** torch.randint(-2, 2, (B, T_kv))).to(torch.float32)
+        kdev, sdev = kk.view(torch.uint8).cuda(), scale.cuda()
+    else:
+        kk = kf.to(torch.bfloat16)
+        kdev, sdev, scale = kk.cuda(), None, None
+    S, idx = gpu_indexer(q.cuda(), kdev, w.cuda(), k, q_pos0, k_scale=sdev)
+    rows = check_rows(T_q)
+    pos = np.array([q_pos0 + t for t in rows])
+    for b in range(B):
+        keys = bytes_u8(kk[b]) if fp8 else bits(kk[b])
+        rS, ridx = oracle.score_select(bits(q[b, rows]), w[b, rows].numpy(), keys, pos, k,
+                                       k_scale=scale[b].numpy() if fp8 else None)
+        for i, t in enumerate(rows):
+            n = q_pos0 + t + 1
+            assert np.array_equal(S[b, t, :n], rS[i, :n]), f"b={b} t={t}: scores differ"
+            assert np.array_equal(idx[b, t], ridx[i]), f"b={b} t={t}: indices differ"
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_score_gaussian(shape, fp8):
+    B, T_q, T_kv, q_pos0, H, D, k = shape
+    log(f"[score-gauss] shape={shape} fp8={fp8}")
+    base = inputs.WORKLOADS["prefill1m" if fp8 else "prefill200k"]
+    wl = dataclasses.replace(base, name=f"t{shape}", B=B, T_q=T_q, n_q=T_q, q_pos0=q_pos0,
+                             T_kv=T_kv, H_I=H, D_I=D, top_k=k)
+    x = inputs.indexer_inputs(wl, 0, "cpu")
+    S, idx = gpu_indexer(x["q"].cuda(), x["k"].cuda(), x["w"].cuda(), k, q_pos0,
+                         k_scale=x["k_scale"].cuda() if fp8 else None)
+    rows = check_rows(T_q)
+    pos = np.array([q_pos0 + t for t in rows])
+    swaps = 0
+    for b in range(B):
+        keys = bytes_u8(x["k"][b]) if fp8 else bits(x["k"][b])
+        rS, ridx = oracle.score_select(bits(x["q"][b, rows]), x["w"][b, rows].numpy(), keys, pos, k,
+                                       k_scale=x["k_scale"][b].numpy() if fp8 else None)
+        for i, t in enumerate(rows):
+            n = q_pos0 + t + 1
+            check_scores(S[b, t, :n], rS[i, :n], f"b={b} t={t}")
+            swaps += check_index_sets(idx[b, t], ridx[i], rS[i, :n], k, f"b={b} t={t}")
+    log(f"  near-tie swaps: {swaps}")
+
+
+def test_score_weight_scaling_and_h1_identity():
+    """Scaling w by 2 doubles every GPU score exactly and keeps the indices."""
+    B, T_q, T_kv, q_pos0, H, D, k = 1, 40, 3000, 2960, 64, 128, 300
+    g = torch.Generator().manual_seed(5)
+    q = (torch.randn(B, T_q, H, D, generator=g) / 8).to(torch.bfloat16).cuda()
+    kk = (torch.randn(B, T_kv, D, generator=g) / 8).to(torch.bfloat16).cuda()
+    w = torch.rand(B, T_q, H, generator=g).cuda()
+    S1, i1 = gpu_indexer(q, kk, w, k, q_pos0)
+    S2, i2 = gpu_indexer(q, kk, 2 * w, k, q_pos0)
+    for t in range(T_q):
+        n = q_pos0 + t + 1
+        assert np.array_equal(S2[0, t, :n], 2 * S1[0, t, :n])
+    assert np.array_equal(i1, i2)
+
+
+def test_prefill_and_splitkey_kernels_agree_bitwise():
+    """The same rows scored as one batch of many rows (prefill kernel) and as
+    single-row calls (split-key kernel) give identical bits: chunking never
+    changes a score."""
+    T_kv, H, D, k = 6000, 64, 128, 512
+    g = torch.Generator().manual_seed(9)
+    T_q, q_pos0 = 2048, T_kv - 2048   # 256 workgroups: the prefill kernel
+    q = (torch.randn(1, T_q, H, D, generator=g) / 8).to(torch.bfloat16).cuda()
+    kk = (torch.randn(1, T_kv, D, generator=g) / 8).to(torch.bfloat16).cuda()
+    w = torch.rand(1, T_q, H, generator=g).cuda()
+    S_all, i_all = gpu_indexer(q, kk, w, k, q_pos0)
+    for t in (0, 17, 1000, 2047):
+        S1, i1 = gpu_indexer(q[:, t:t + 1], kk, w[:, t:t + 1], k, q_pos0 + t)
+        n = q_pos0 + t + 1
+        assert np.array_equal(S1[0, 0, :n], S_all[0, t, :n])
+        assert np.array_equal(i1[0, 0], i_all[0, t])
