@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from long_context_sparse_idx_amd import inputs, lcsi  # noqa: E402
+from long_context_sparse_idx_amd.runner import Workload, pairs_in_chunk  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -40,81 +41,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class Path:
-    """Device-resident inputs and outputs of one workload."""
-
-    def __init__(self, wl, all_f_inputs: bool):
-        self.wl = wl
-        dev = "cuda"
-        L = wl.n_layers
-        self.f_layers = [l for l in range(L) if wl.pattern[l]]
-        need_f = list(range(L)) if all_f_inputs else self.f_layers
-        t0 = time.time()
-        self.idx_in = {l: inputs.indexer_inputs(wl, l, dev) for l in need_f}
-        self.attn_in = [inputs.attn_inputs(wl, l, dev) for l in range(L)]
-        self.outs = [torch.empty((wl.B, wl.n_q, wl.H_q, wl.D_v), dtype=torch.bfloat16, device=dev)
-                     for _ in range(L)]
-        self.cache = torch.empty((1, wl.B, wl.n_q, wl.top_k), dtype=torch.int32, device=dev)
-        torch.cuda.synchronize()
-        log(f"[bench] inputs for {wl.name} ready in {time.time() - t0:.1f}s")
-        self.tau = inputs.sm_scale(wl)
-        self.ws = None
-        self.ws_bytes = 0
-
-    def chunk_descs(self, q0, tq, T_kv, pattern):
-        wl = self.wl
-        f_idx = [l for l in range(len(pattern)) if pattern[l]]
-        ids = []
-        for l in f_idx:
-            x = self.idx_in[l]
-            ids.append(lcsi.indexer_desc(x["q"][:, q0 - wl.q_pos0:q0 - wl.q_pos0 + tq], x["k"],
-                                         x["w"][:, q0 - wl.q_pos0:q0 - wl.q_pos0 + tq], wl.top_k, q0,
-                                         k_scale=x["k_scale"], T_kv=T_kv))
-        ads = []
-        for l in range(len(pattern)):
-            x = self.attn_in[l]
-            r0 = q0 - wl.q_pos0
-            ads.append(lcsi.attn_desc(x["q"][:, r0:r0 + tq], x["k"], x["v"], self.outs[l][:, r0:r0 + tq],
-                                      wl.top_k, q0, self.tau, T_kv=T_kv))
-        return ids, ads
-
-    def plan(self, pattern):
-        """Per-chunk descriptors and the shared workspace."""
-        wl = self.wl
-        plans = []
-        need = 0
-        for (q0, tq, T_kv) in wl.chunks():
-            ids, ads = self.chunk_descs(q0, tq, T_kv, pattern)
-            cache = self.cache[:, :, q0 - wl.q_pos0:]
-            n = lcsi.layer_group_ws_bytes(pattern, ids, ads, cache, 1, 0, wl.n_q * wl.top_k, wl.top_k)
-            need = max(need, n)
-            plans.append((q0, tq, T_kv, ids, ads, cache))
-        if need > self.ws_bytes:
-            self.ws = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
-            self.ws_bytes = need
-        return plans
-
-    def step(self, pattern, plans, events=None):
-        wl = self.wl
-        for c, (q0, tq, T_kv, ids, ads, cache) in enumerate(plans):
-            ev = events[c] if events is not None else None
-            lcsi.run_layer_group(pattern, ids, ads, cache, 1, 0, wl.n_q * wl.top_k, wl.top_k,
-                                 ws=self.ws, events=ev)
+def score_traffic(wl):
+    """HBM bytes per score launch from the committed counter runs, or None
+    when the score kernel source changed since they were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "score_traffic.json")) as f:
+            t = json.load(f)
+        with open(os.path.join(ROOT, "long_context_sparse_idx_amd", "csrc", "score.hip"), "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if t.get("source_sha256") != h or t.get("workload") != wl.name:
+        return None
+    return t["bytes_per_launch"]
 
 
-def pairs_in_chunk(q0, tq):
-    """Causal (query, key) pairs of rows q0 .. q0+tq-1."""
-    return tq * (q0 + 1) + tq * (tq - 1) // 2
-
-
-def cpu_baseline(path: Path, max_rows: int | None = None):
+def cpu_baseline(path: Workload, max_rows: int | None = None):
     """The oracle's indexer + top-k on a bounded, evenly spaced sample of rows."""
     import oracle
     wl = path.wl
     threads = oracle.default_threads()
-    R = max_rows or max(4, 2 * threads)
+    R = max_rows or max(8, 4 * threads)
     pos = np.array([wl.q_pos0 + int((i + 0.5) * wl.n_q / R) for i in range(R)], np.int64)
-    l = path.f_layers[0]
+    l = path.pattern_f[0]
     x = path.idx_in[l]
     rows = torch.from_numpy(pos - wl.q_pos0).cuda()
     q = x["q"][0].index_select(0, rows).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -141,23 +91,34 @@ def main():
     ap.add_argument("--workload", default="prefill200k", choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-allf", action="store_true", help="skip the all-F comparison pass")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
               "multi-GPU mode in this build", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)          # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy of 1 GiB done")
     wl = inputs.WORKLOADS[args.workload]
-    path = Path(wl, all_f_inputs=not args.no_allf)
+    path = Workload(wl, f_layers=range(wl.n_layers) if not args.no_allf else None, log=log)
     pattern = wl.pattern
-    plans = path.plan(pattern)
+    plan = path.plan(pattern)
+    plans = plan[1]
     L = wl.n_layers
     nchunk = len(plans)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] for _ in range(nchunk)]
     stream = torch.cuda.current_stream()
 
     for i in range(args.warmup):
-        path.step(pattern, plans)
+        path.step(plan)
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
 
@@ -168,7 +129,7 @@ def main():
     for i in range(args.steps):
         s0 = torch.cuda.Event(enable_timing=True)
         s0.record(stream)
-        path.step(pattern, plans, events)
+        path.step(plan, events)
         torch.cuda.synchronize()
         sc = se = at = 0.0
         for c in range(nchunk):
@@ -200,7 +161,8 @@ def main():
     score_s = float(np.mean(score_ms)) / 1e3
     achieved = pairs * flops_per_pair * n_f / score_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": score_traffic(wl),
                 "kernel": "score_prefill_kernel<64,128,bf16>",
                 "launches_per_step": nchunk * n_f,
                 "avg_launch_ms": round(float(np.mean(score_ms)) / (nchunk * n_f), 4)}
@@ -215,13 +177,13 @@ def main():
     extra = {}
     if not args.no_allf:
         allf = tuple(1 for _ in range(L))
-        plans_f = path.plan(allf)
-        path.step(allf, plans_f)
+        plan_f = path.plan(allf)
+        path.step(plan_f)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev_f = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] for _ in range(nchunk)]
         e0.record(stream)
-        path.step(allf, plans_f, ev_f)
+        path.step(plan_f, ev_f)
         e1.record(stream)
         torch.cuda.synchronize()
         allf_ms = e0.elapsed_time(e1)
