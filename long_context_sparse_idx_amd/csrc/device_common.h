@@ -71,6 +71,17 @@ __device__ __forceinline__ uint32_t order_key(float x)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// x[lane] + x[lane ^ 32], formed as (lower half + upper half) in every lane,
+// with v_permlane32_swap (a VALU op: no LDS traffic, no lgkmcnt wait).  With
+// old = src = x the swap returns, in every lane, the lower-half value in
+// element 0 and the upper-half value in element 1.
+__device__ __forceinline__ float sum_lane_halves(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll

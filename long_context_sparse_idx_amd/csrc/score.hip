@@ -35,7 +35,6 @@ namespace {
 
 constexpr int WAVES_PREFILL = 8;  // 512 threads: 2 waves per SIMD
 constexpr int WAVES_SPLIT = 4;
-constexpr int KT = 64;            // keys per LDS tile (two 32-key MFMA blocks)
 
 template <int D>
 struct KeyGeom {
@@ -75,35 +74,49 @@ struct WaveRows {
     }
 };
 
-// ReLU * weight, head reduction and the store of one 32-key block.
-// Summation order is fixed (rt, then r ascending, then the lane-pair add),
-// so every kernel that calls this produces bit-identical scores.
+// Epilogue of one 32-key block: ReLU * weight and the head reduction
+// (epi_reduce, pure register arithmetic), then the store (epi_store).  The
+// summation order is fixed (row tile, then r ascending, then the lane-pair
+// add), so every kernel that calls these produces bit-identical scores.
 template <int H>
-__device__ __forceinline__ void score_epilogue(const f32x16 &acc0, const f32x16 &acc1, const float (&wl)[2][16],
-                                               float kscale, float *Sb, int64_t ld, int T_q, int tq0, int key,
-                                               int lane)
+struct Part {
+    static constexpr int N = H >= 8 ? 64 / H : 8;
+    float v[N];
+};
+
+template <int H>
+__device__ __forceinline__ Part<H> epi_reduce(const f32x16 &acc0, const f32x16 &acc1, const float (&wl)[2][16],
+                                              float kscale)
 {
-    const int g = lane >> 5;
+    Part<H> p;
     if constexpr (H >= 8) {
+        // Each query owns E = 32/QPW accumulator values of this lane; they are
+        // summed into NP independent partial sums (element e goes to partial
+        // e % NP) and the partials are added as a balanced tree, so the VALU
+        // never waits on one long dependent chain.
         constexpr int QPW = 64 / H;
-        float part[QPW];
+        constexpr int E = 32 / QPW;
+        constexpr int NP = E >= 16 ? 8 : (E >= 8 ? 4 : 2);
+        float ps[QPW][NP];
 #pragma unroll
-        for (int q = 0; q < QPW; ++q) part[q] = 0.f;
+        for (int q = 0; q < QPW; ++q)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part[(8 * (r >> 2)) / H] += wl[0][r] * fmaxf(acc0[r], 0.f);
+            for (int j = 0; j < NP; ++j) ps[q][j] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part[(32 + 8 * (r >> 2)) / H] += wl[1][r] * fmaxf(acc1[r], 0.f);
+        for (int r = 0; r < 32; ++r) {
+            const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2);  // first row of r's group of 4
+            const int q = row / H;
+            const int e = r - q * E;                               // element index within query q
+            const float x = r < 16 ? acc0[r] : acc1[r - 16];
+            ps[q][e % NP] += wl[r >> 4][r & 15] * fmaxf(x, 0.f);
+        }
 #pragma unroll
-        for (int q = 0; q < QPW; ++q) part[q] = (part[q] + __shfl_xor(part[q], 32)) * kscale;
-        if constexpr (QPW == 1) {
-            if (g == 0 && tq0 < T_q) Sb[(int64_t)tq0 * ld + key] = part[0];
-        } else {
+        for (int q = 0; q < QPW; ++q) {
 #pragma unroll
-            for (int q = 0; q < QPW; ++q) {
-                const bool mine = (q < QPW / 2) == (g == 0);
-                const int t = tq0 + q;
-                if (mine && t < T_q) Sb[(int64_t)t * ld + key] = part[q];
-            }
+            for (int w = NP / 2; w >= 1; w >>= 1)
+#pragma unroll
+                for (int j = 0; j < w; ++j) ps[q][j] += ps[q][j + w];
+            p.v[q] = sum_lane_halves(ps[q][0]) * kscale;
         }
     } else {
         static_assert(H == 4, "H must be 4, 8, 16, 32 or 64");
@@ -116,8 +129,36 @@ __device__ __forceinline__ void score_epilogue(const f32x16 &acc0, const f32x16 
                 float v = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v += wl[rt][4 * j + i] * fmaxf(acc[4 * j + i], 0.f);
+                p.v[rt * 4 + j] = v * kscale;
+            }
+        }
+    }
+    return p;
+}
+
+template <int H>
+__device__ __forceinline__ void epi_store(const Part<H> &p, float *Sb, int64_t ld, int T_q, int tq0, int key, int lane)
+{
+    const int g = lane >> 5;
+    if constexpr (H >= 8) {
+        constexpr int QPW = 64 / H;
+        if constexpr (QPW == 1) {
+            if (g == 0 && tq0 < T_q) Sb[(int64_t)tq0 * ld + key] = p.v[0];
+        } else {
+#pragma unroll
+            for (int q = 0; q < QPW; ++q) {
+                const bool mine = (q < QPW / 2) == (g == 0);
+                const int t = tq0 + q;
+                if (mine && t < T_q) Sb[(int64_t)t * ld + key] = p.v[q];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
                 const int t = tq0 + rt * 8 + 2 * j + g;
-                if (t < T_q) Sb[(int64_t)t * ld + key] = v * kscale;
+                if (t < T_q) Sb[(int64_t)t * ld + key] = p.v[rt * 4 + j];
             }
         }
     }
@@ -151,6 +192,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     constexpr int QPW = 64 / H;
     constexpr int QPB = WAVES_PREFILL * QPW;
     constexpr int NT = WAVES_PREFILL * 64;
+    constexpr int KT = 64;  // keys per LDS tile (two 32-key MFMA blocks)
     // 16-byte chunks of one tile as stored in LDS (bf16) and as read from HBM
     constexpr int SRC_CHUNK_KEY = FP8 ? D / 16 : D / 8;   // per key
     constexpr int SRC_CHUNKS = KT * SRC_CHUNK_KEY;
@@ -211,6 +253,13 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     };
 
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
+    // Software pipeline inside each wave: while the MFMAs of block j run, the
+    // VALU reduces block j-1 (its accumulators wait in pa0/pa1), so the
+    // matrix and vector units overlap within one wave as well as across the
+    // two waves of a SIMD.
+    f32x16 pa0 = f32x16{0}, pa1 = f32x16{0};
+    int pkey = -1;
+    float pks = 1.f;
     fetch(0);
     stash(0);
     __syncthreads();
@@ -218,19 +267,32 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         const int buf = it & 1;
         if (it + 1 < ntiles) fetch(it + 1);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < KT / 32; ++cb) {
             const uint8_t *src = sk[buf] + (cb * 32 + l32) * G::ROWB + g * G::HALF * 2;
             bf16x8 bk[G::KSTEPS];
 #pragma unroll
             for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
+            const float ksc = FP8 ? ssc[buf][cb * 32 + l32] : 1.f;
             f32x16 acc0, acc1;
             mfma_block<D>(rows.qa, bk, acc0, acc1);
-            const float ksc = FP8 ? ssc[buf][cb * 32 + l32] : 1.f;
-            score_epilogue<H>(acc0, acc1, rows.wl, ksc, Sb, a.ld, a.T_q, tq0, it * KT + cb * 32 + l32, lane);
+            const Part<H> pp = epi_reduce<H>(pa0, pa1, rows.wl, pks);
+            // shape: the B-fragment reads, then MFMAs interleaved with VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, G::KSTEPS, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * G::KSTEPS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            if (pkey >= 0) epi_store<H>(pp, Sb, a.ld, a.T_q, tq0, pkey, lane);
+            pa0 = acc0;
+            pa1 = acc1;
+            pkey = it * KT + cb * 32 + l32;
+            pks = ksc;
         }
         if (it + 1 < ntiles) stash(buf ^ 1);
         __syncthreads();
     }
+    if (pkey >= 0) epi_store<H>(epi_reduce<H>(pa0, pa1, rows.wl, pks), Sb, a.ld, a.T_q, tq0, pkey, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -292,7 +354,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
         f32x16 acc0, acc1;
         mfma_block<D>(rows.qa, bk, acc0, acc1);
         const int64_t key = key_lo + (int64_t)blk * 32 + l32;
-        score_epilogue<H>(acc0, acc1, rows.wl, cs, Sb, a.ld, a.T_q, tq0, (int)key, lane);
+        epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), Sb, a.ld, a.T_q, tq0, (int)key, lane);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) cur[i] = nxt[i];
         cs = ns;
