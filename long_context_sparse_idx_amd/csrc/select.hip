@@ -13,7 +13,7 @@
 // to K* are taken; a stable, wave-ordered compaction then writes every entry
 // with key > K* and the first `need` entries with key == K*.
 //
-// One 1024-thread workgroup per row, three paths:
+// One 512-thread workgroup per row, three paths:
 //  A  n <= 16384: the whole row's keys sit in LDS; select there.
 //  B  longer rows: 8192 sampled scores (32 evenly spaced runs of 256) give
 //     a threshold tau expected to pass ~2.5k entries; one streaming pass
@@ -29,13 +29,14 @@ namespace lcsi {
 
 namespace {
 
-constexpr int NT = 1024;
+constexpr int NT = 512;
 constexpr int NW = NT / 64;
 constexpr int NLDS = 16384;       // path A limit
-constexpr int CAPW = 512;         // candidate slots per wave (path B)
+constexpr int CAPW = 1024;        // candidate slots per wave (path B)
 constexpr int NSB = 32;           // sample runs
 constexpr int SBL = 256;          // run length
 constexpr int NSAMP = NSB * SBL;
+constexpr int NSUB = 4;           // histogram copies (waves w and w+4k share one)
 
 struct Shared {
     union {
@@ -46,12 +47,13 @@ struct Shared {
             int32_t idx[NW * CAPW];
         } cand;                                  // path B candidates
     } u;
-    uint32_t hist[256];
+    uint32_t hist[NSUB][256];
     int wcnt[NW];
     int wgt[NW];
     int wtie[NW];
     uint32_t kth;
     int rem;
+    uint32_t kmin, kmax;
 };
 
 // ---- element visitors: each thread calls f(key) for its share ------------
@@ -93,24 +95,76 @@ struct GlobalRow {
 // Find the rank-th largest key (rank >= 1, at most the number of visited
 // keys).  On return sh.kth is that key and sh.rem the number of entries
 // equal to it that belong to the top `rank`.
+//
+// A first pass finds the smallest and largest key; the 8-bit digit passes
+// then run on the offset key - kmin, starting at the highest bit of the
+// range kmax - kmin, so the first 256 bins span the keys actually present
+// (scores of one row share sign and exponent bits, and a digit over those
+// bits would put nearly every key into one or two bins).
+// resolve < 32 stops once that many offset bits from the top are fixed:
+// sh.kth is then kmin + the offset prefix with the lower bits cleared -- a
+// lower bound of the rank-th key that at least `rank` keys reach (used for
+// the sampled threshold, where only a bound is needed).
 template <class Src>
-__device__ void radix_find(Shared &sh, const Src &src, int rank)
+__device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 32)
 {
-    const int tid = threadIdx.x, lane = tid & 63;
-    uint32_t prefix = 0, mask = 0;
-    int rem = rank;
-#pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) sh.hist[tid] = 0;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) {
+        sh.kmin = 0xFFFFFFFFu;
+        sh.kmax = 0u;
+    }
+    __syncthreads();
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    src.visit([&](uint32_t key) {
+        kmn = min(kmn, key);
+        kmx = max(kmx, key);
+    });
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmn = min(kmn, (uint32_t)__shfl_xor(kmn, o));
+        kmx = max(kmx, (uint32_t)__shfl_xor(kmx, o));
+    }
+    if (lane == 0) {
+        atomicMin(&sh.kmin, kmn);
+        atomicMax(&sh.kmax, kmx);
+    }
+    __syncthreads();
+    const uint32_t kmin = sh.kmin, range = sh.kmax - kmin;
+    if (range == 0) {  // all keys equal: the rank-th is that key
+        if (tid == 0) {
+            sh.kth = kmin;
+            sh.rem = rank;
+        }
         __syncthreads();
+        return;
+    }
+    const int msb = 31 - __builtin_clz(range);
+    uint32_t mask = msb == 31 ? 0u : ~((2u << msb) - 1u);  // offset bits already fixed (all zero)
+    uint32_t prefix = 0;                                    // fixed offset bits
+    int rem = rank;
+    int hi = msb;  // highest bit of the next digit
+#pragma unroll 1
+    while (true) {
+        const int shift = hi >= 7 ? hi - 7 : 0;
+        const uint32_t dmask = (2u << (hi - shift)) - 1u;  // digit width hi-shift+1 <= 8 bits
+        for (int i = tid; i < NSUB * 256; i += NT) (&sh.hist[0][0])[i] = 0;
+        __syncthreads();
+        uint32_t *hw = sh.hist[w % NSUB];
         src.visit([&](uint32_t key) {
-            if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+            const uint32_t off = key - kmin;
+            if ((off & mask) == prefix) atomicAdd(&hw[(off >> shift) & dmask], 1u);
         });
         __syncthreads();
         if (tid < 64) {
-            const uint32_t c0 = sh.hist[4 * lane], c1 = sh.hist[4 * lane + 1];
-            const uint32_t c2 = sh.hist[4 * lane + 2], c3 = sh.hist[4 * lane + 3];
-            const int tot = (int)(c0 + c1 + c2 + c3);
+            uint32_t c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int h = 0; h < NSUB; ++h) v += sh.hist[h][4 * lane + e];
+                c[e] = v;
+            }
+            const int tot = (int)(c[0] + c[1] + c[2] + c[3]);
             int suf = tot;  // inclusive suffix sum over lanes >= this one
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -119,7 +173,6 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank)
             }
             const int above = suf - tot;
             if (above < rem && rem <= suf) {
-                const uint32_t c[4] = {c0, c1, c2, c3};
                 int acc = above;
                 for (int e = 3; e >= 0; --e) {
                     if (acc + (int)c[e] >= rem) {
@@ -134,8 +187,13 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank)
         __syncthreads();
         prefix = sh.kth;
         rem = sh.rem;
-        mask |= 0xFFu << shift;
+        mask |= dmask << shift;
+        if (shift == 0 || msb - shift + 1 >= resolve) break;
+        hi = shift - 1;
     }
+    __syncthreads();  // every thread has read sh.kth / sh.rem above
+    if (tid == 0) sh.kth = kmin + prefix;
+    __syncthreads();
 }
 
 // Ordered compaction over per-wave segments visited in ascending position
@@ -260,7 +318,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 
     // ---- path B: sampled threshold, one streaming pass, exact select on
     // the candidates
-    for (int s = 2 * w; s < 2 * w + 2; ++s) {
+    for (int s = w * (NSB / NW); s < (w + 1) * (NSB / NW); ++s) {
         const int64_t start = ((n - SBL) * s / (NSB - 1)) & ~(int64_t)3;
         const f32x4 v = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
         uint32_t *d = sh.u.samp + s * SBL + 4 * lane;
@@ -272,7 +330,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     __syncthreads();
     int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
     r = r < 1 ? 1 : (r > NSAMP ? NSAMP : r);
-    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r);
+    // a lower bound of the r-th sampled key, resolved to 1/256 of the
+    // samples' key range, is precise enough for a threshold
+    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r, 8);
     const uint32_t tau = sh.kth;
     __syncthreads();  // every thread has read tau before the lists overwrite the samples
 
