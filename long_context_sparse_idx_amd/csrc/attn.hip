@@ -11,17 +11,21 @@
 //
 // One workgroup (4 waves) = one query row (and one split of its index list
 // when few rows are present).  Per tile of 32 indices:
-//   gather  : the 32 KV rows are read once from HBM; the K part is stored
-//             row-major in LDS and the V part transposed (V^T[dim][key]) so
-//             the PV product can read 8 consecutive keys of one dim at once.
+//   gather  : the 32 KV rows go straight from HBM into LDS with direct
+//             global->LDS loads (no staging registers), one tile ahead of the
+//             compute, into a double-buffered row-major tile; one gathered
+//             row serves as both K and V when V is the first D_v columns of
+//             the K row.
 //   S^T     : 16x16x32 bf16 MFMA with K as the A operand (16 keys) and Q^T
 //             as B (16 heads), so a lane ends up holding 8 keys of ONE head.
 //             The A-row -> key map is chosen so those 8 keys are consecutive
 //             (8g .. 8g+7 for lane group g).
 //   softmax : online, in fp32 registers, exp2 with the scale folded in.
-//   PV      : O^T = V^T P^T: A from LDS V^T, B = the lane's own 8 p values
-//             packed to bf16 -- P never leaves registers; O^T's layout keeps
-//             one head per lane, matching the softmax state.
+//   PV      : O^T = V^T P^T: the A operand (8 consecutive keys of one V
+//             column) comes from the row-major tile through LDS transpose
+//             reads; B = the lane's own 8 p values packed to bf16 -- P never
+//             leaves registers; O^T's layout keeps one head per lane,
+//             matching the softmax state.
 // Each wave owns 16 heads and DV/NDS output dims (NDS = 4 / head groups).
 #include "device_common.h"
 #include "kernels.h"
@@ -30,8 +34,9 @@ namespace lcsi {
 
 namespace {
 
-constexpr int TK = 32;           // indices per tile
-constexpr int VTROW = TK * 2 + 16;  // LDS bytes per V^T row (+16 B pad)
+constexpr int TK = 32;  // indices per tile
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int32_t usable_index(const AttnArgs &a, const int32_t *row, int j, int j_hi, int64_t p)
 {
@@ -40,20 +45,58 @@ __device__ __forceinline__ int32_t usable_index(const AttnArgs &a, const int32_t
     return (v >= 0 && v <= p && v < a.T_kv) ? v : -1;
 }
 
-template <int DQK, int DV, int NDS>
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i names 8 bytes M[i][0..3] (four b16 values) and lane j receives
+// M[4e + j/4][j%4] for e = 0..3.  With lane i pointing at row kb + i/4,
+// columns db + 4(i%4) of a row-major tile, lane j gets column db + j of rows
+// kb .. kb+3.
+// (The builtin is only spelled out for the device pass: in the host pass of
+// the same source an LDS builtin on a computed pointer suppresses the
+// host-side launch stub of the kernel that calls it, and a __device__
+// function never runs on the host.)
+__device__ __forceinline__ uint2 lds_read_tr(const uint8_t *p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint8_t *>(p)));
+    return __builtin_bit_cast(uint2, v);
+#else
+    (void)p;
+    return uint2{0, 0};
+#endif
+}
+
+// Direct global->LDS load (global_load_lds_dwordx4): every lane loads 16
+// bytes from its own address; lane l's bytes land at lds + 16*l (lds is
+// wave-uniform).  Device pass only, as above.
+__device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+    (void)src;
+    (void)lds;
+#endif
+}
+
+template <int DQK, int DV, int NDS, bool SHARED>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 {
-    constexpr int KROW = DQK * 2 + 16;     // LDS bytes per K row (+16 B pad)
-    constexpr int NCK = DQK / 8;           // 16-byte chunks per K row
-    constexpr int NCV = DV / 8;            // 16-byte chunks of V per row
+    // Row-major KV tile in LDS: each row holds the K row (DQK bf16) and, when
+    // V is a separate tensor, the V row after it, plus one 16-byte pad slot.
+    constexpr int NCK = DQK / 8;                      // 16-byte chunks of a K row
+    constexpr int NCV = SHARED ? 0 : DV / 8;          // chunks of a separate V row
+    constexpr int RS = NCK + NCV + 1;                 // 16-byte slots per LDS row
+    constexpr int ROWB = RS * 16;
+    constexpr int VOFF = SHARED ? 0 : DQK * 2;        // byte offset of V within a row
+    constexpr int NDMA = (TK * RS + 63) / 64;         // 1 KB direct loads per tile
+    constexpr int BUFB = NDMA * 1024;                 // bytes per tile buffer
     constexpr int QSTEPS = DQK / 32;
-    constexpr int NWH = 4 / NDS;           // head groups of 16
-    constexpr int DVW = DV / NDS;          // output dims per wave
+    constexpr int NWH = 4 / NDS;                      // head groups of 16
+    constexpr int DVW = DV / NDS;                     // output dims per wave
     constexpr int NDT = DVW / 16;
 
-    __shared__ __attribute__((aligned(16))) uint8_t sk[TK * KROW];
-    __shared__ __attribute__((aligned(16))) uint8_t svt[DV * VTROW];
-    __shared__ int32_t sidx[2][TK];
+    __shared__ __attribute__((aligned(1024))) uint8_t kv[2][BUFB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
@@ -67,7 +110,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const int32_t *irow = a.idx + (int64_t)b * a.idx_sb + (int64_t)t * a.idx_st;
     const uint16_t *kbase = a.k + (int64_t)b * a.k_sb;
     const uint16_t *vbase = a.v + (int64_t)b * a.v_sb;
-    const bool shared_kv = a.v == a.k && a.v_st == a.k_st;
 
     // Q^T fragments (B operand): head l16 of this wave's group, 8 dims of group g per k-step
     bf16x8 qf[QSTEPS];
@@ -82,53 +124,53 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0, 0, 0, 0};
     float m_run = -__builtin_inff(), l_run = 0.f;
 
-    if (tid < TK) sidx[0][tid] = usable_index(a, irow, j_lo + tid, j_hi, p);
-    __syncthreads();
+    // ---- index handling: lanes l and l+32 of every wave hold entry l of a
+    // tile's index list (usable index or -1).  The raw entries of tile it+2
+    // are loaded while tile it computes, so no load waits on them.
+    auto raw_idx = [&](int tile) -> int32_t {
+        const int j = j_lo + tile * TK + (lane & 31);
+        return (tile < ntile && j < j_hi) ? irow[j] : -1;
+    };
+    auto usable = [&](int32_t v) -> int32_t { return (v >= 0 && v <= p && v < a.T_kv) ? v : -1; };
+    // ---- gather: direct global->LDS loads of one tile (wave w issues loads
+    // w, w+4, ...; lane l of load m fills 16-byte slot 64m + l, which is
+    // chunk c of tile row r).  Unusable indices read row 0 instead (finite
+    // data; their keys are masked), pad slots and slots past the tile
+    // re-read the row's first chunk.
+    auto gather = [&](int32_t keys, int buf) {
+#pragma unroll
+        for (int m = wave; m < NDMA; m += 4) {
+            const int slot = 64 * m + lane;
+            const int row = slot / RS, c = slot - row * RS;
+            const int32_t key = __shfl(keys, row < TK ? row : 0);
+            const int64_t kr = (row < TK && key >= 0) ? key : 0;
+            const uint16_t *src = c < NCK ? kbase + kr * a.k_st + 8 * c
+                                 : (c < NCK + NCV ? vbase + kr * a.v_st + 8 * (c - NCK) : kbase + kr * a.k_st);
+            load_to_lds16(src, kv[buf] + 1024 * m);
+        }
+    };
 
+    const int32_t keys0 = usable(raw_idx(0));
+    int32_t raw_next = raw_idx(1);
+    gather(keys0, 0);
+    uint32_t vmask = (uint32_t)__ballot(keys0 >= 0);  // bit r: tile row r usable
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     for (int it = 0; it < ntile; ++it) {
         const int buf = it & 1;
-        // ---- gather the tile: items (chunk c, group of 4 rows rg)
-        {
-            const int nitems = (shared_kv ? NCK : NCK + NCV) * (TK / 4);
-            for (int item = tid; item < nitems; item += 256) {
-                const int c = item >> 3, rg = item & 7;
-                const bool kpart = c < NCK;
-                const int cc = kpart ? c : c - NCK;      // chunk within its tensor
-                const uint16_t *src = kpart ? kbase : vbase;
-                const int64_t sst = kpart ? a.k_st : a.v_st;
-                u32x4 v[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int32_t key = sidx[buf][4 * rg + i];
-                    v[i] = key >= 0 ? ld16(src + (int64_t)key * sst + 8 * cc) : u32x4{0, 0, 0, 0};
-                }
-                if (kpart) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) st16(sk + (4 * rg + i) * KROW + 16 * cc, v[i]);
-                }
-                const bool vpart = shared_kv ? (kpart && cc < NCV) : !kpart;
-                if (vpart) {
-                    // transpose 4 rows x 8 dims -> 8 dims x 4 rows
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const uint32_t x0 = v[0][m], x1 = v[1][m], x2 = v[2][m], x3 = v[3][m];
-                        const u32x2 lo{(x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16)};
-                        const u32x2 hi{(x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u)};
-                        *reinterpret_cast<u32x2 *>(svt + (8 * cc + 2 * m) * VTROW + 8 * rg) = lo;
-                        *reinterpret_cast<u32x2 *>(svt + (8 * cc + 2 * m + 1) * VTROW + 8 * rg) = hi;
-                    }
-                }
-            }
-        }
-        if (tid < TK && it + 1 < ntile) sidx[buf ^ 1][tid] = usable_index(a, irow, j_lo + (it + 1) * TK + tid, j_hi, p);
-        const int any = __syncthreads_or(tid < TK && sidx[buf][tid] >= 0);
+        const int32_t keys_next = usable(raw_next);
+        raw_next = raw_idx(it + 2);
+        if (it + 1 < ntile) gather(keys_next, buf ^ 1);
+        const uint32_t vcur = (vmask >> (8 * g)) & 0xFFu;  // this lane's keys 8g .. 8g+7
+        const bool any = vmask != 0;
         if (any) {
+            const uint8_t *tb = kv[buf];
             // ---- S^T = K Q^T for 32 keys (two 16-key halves)
             f32x4 sacc[2];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int krow = 8 * (l16 >> 2) + 4 * hf + (l16 & 3);
-                const uint8_t *kp = sk + krow * KROW + 16 * g;
+                const uint8_t *kp = tb + krow * ROWB + 16 * g;
                 f32x4 acc{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < QSTEPS; ++s)
@@ -141,7 +183,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             float mt = -__builtin_inff();
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const bool ok = sidx[buf][8 * g + e] >= 0;
+                const bool ok = (vcur >> e) & 1u;
                 sv[e] = ok ? sacc[e >> 2][e & 3] * a.sm_scale_log2 : -__builtin_inff();
                 mt = fmaxf(mt, sv[e]);
             }
@@ -165,16 +207,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             l_run = l_run * alpha + psum;
 #pragma unroll
             for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
-            const bf16x8 pf = as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                              pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
-            // ---- O^T += V^T P^T
-            const uint8_t *vp = svt + (ds * DVW + l16) * VTROW + 16 * g;
+            const bf16x8 pfv = as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                               pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+            // ---- O^T += V^T P^T; A = column (ds*DVW + dt*16 + l16) of rows 8g .. 8g+7
+            const uint8_t *vp = tb + (8 * g + (l16 >> 2)) * ROWB + VOFF + 2 * (ds * DVW + 4 * (l16 & 3));
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + dt * 16 * VTROW)), pf, oacc[dt], 0, 0, 0);
+            for (int dt = 0; dt < NDT; ++dt) {
+                const uint2 lo = lds_read_tr(vp + 32 * dt);
+                const uint2 hi = lds_read_tr(vp + 4 * ROWB + 32 * dt);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), pfv,
+                                                                   oacc[dt], 0, 0, 0);
+            }
         }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the other buffer have landed
         __syncthreads();
+        vmask = (uint32_t)__ballot(keys_next >= 0);
     }
 
     float l_tot = l_run;
@@ -232,17 +279,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
     }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool SHARED>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(a.splits, a.T_q, a.B);
     const int nwh = (a.H + 15) / 16;
     if (nwh == 1)
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 4>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 4, SHARED>), grid, dim3(256), 0, st, a);
     else if (nwh == 2)
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 2>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, SHARED>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, SHARED>), grid, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.T_q), dim3(256), 0, st, a);
@@ -269,8 +316,11 @@ void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len)
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st)
 {
-    if (a.DQK == 576 && a.DV == 512) return launch_attn_d<576, 512>(a, st);
-    if (a.DQK == 128 && a.DV == 128) return launch_attn_d<128, 128>(a, st);
+    const bool shared = a.v == a.k && a.v_st == a.k_st;
+    if (a.DQK == 576 && a.DV == 512)
+        return shared ? launch_attn_d<576, 512, true>(a, st) : launch_attn_d<576, 512, false>(a, st);
+    if (a.DQK == 128 && a.DV == 128)
+        return shared ? launch_attn_d<128, 128, true>(a, st) : launch_attn_d<128, 128, false>(a, st);
     return hipErrorInvalidValue;
 }
 
