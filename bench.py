@@ -58,29 +58,86 @@ def score_traffic(wl):
 
 
 def cpu_baseline(path: Workload, max_rows: int | None = None):
-    """The oracle's indexer + top-k on a bounded, evenly spaced sample of rows."""
+    """The oracle's indexer + top-k on a bounded sample of rows: evenly
+    spaced query rows of sequence 0 for a prefill workload, the new token of
+    the first few sequences for decode."""
     import oracle
     wl = path.wl
     threads = oracle.default_threads()
-    R = max_rows or max(8, 4 * threads)
-    pos = np.array([wl.q_pos0 + int((i + 0.5) * wl.n_q / R) for i in range(R)], np.int64)
-    l = path.pattern_f[0]
-    x = path.idx_in[l]
-    rows = torch.from_numpy(pos - wl.q_pos0).cuda()
-    q = x["q"][0].index_select(0, rows).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    w = x["w"][0].index_select(0, rows).cpu().numpy()
-    if wl.key_fp8:
-        keys = x["k"][0].cpu().numpy()
-        ks = x["k_scale"][0].cpu().numpy()
-    else:
-        keys = x["k"][0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        ks = None
+    x = path.idx_in[path.pattern_f[0]]
+
+    def seq_arrays(b):
+        if wl.key_fp8:
+            return x["k"][b].cpu().numpy(), x["k_scale"][b].cpu().numpy()
+        return x["k"][b].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), None
+
+    def rows_of(b, rows):
+        r = torch.as_tensor(rows, device=x["q"].device)
+        q = x["q"][b].index_select(0, r).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return q, x["w"][b].index_select(0, r).cpu().numpy()
+
     t0 = time.time()
-    oracle.score_select(q, w, keys, pos, wl.top_k, k_scale=ks, want_scores=False, threads=threads)
+    if wl.n_q > 1:
+        R = max_rows or max(8, 4 * threads)
+        pos = np.array([wl.q_pos0 + int((i + 0.5) * wl.n_q / R) for i in range(R)], np.int64)
+        q, w = rows_of(0, pos - wl.q_pos0)
+        keys, ks = seq_arrays(0)
+        t0 = time.time()
+        oracle.score_select(q, w, keys, pos, wl.top_k, k_scale=ks, want_scores=False, threads=threads)
+        what = f"{R} evenly spaced rows of sequence 0 (positions {pos[0]}..{pos[-1]})"
+    else:
+        R = max_rows or min(wl.B, 4)
+        dt = 0.0
+        for b in range(R):
+            q, w = rows_of(b, [0])
+            keys, ks = seq_arrays(b)
+            t1 = time.time()
+            oracle.score_select(q, w, keys, np.array([wl.q_pos0], np.int64), wl.top_k, k_scale=ks,
+                                want_scores=False, threads=threads)
+            dt += time.time() - t1
+        t0 = time.time() - dt
+        what = f"the new token of sequences 0..{R - 1} (position {wl.q_pos0}), one row per call"
+        threads = 1     # the oracle spreads rows over threads; one row runs on one
     dt = time.time() - t0
     return {"value": R / dt, "unit": "query-tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{R} evenly spaced rows of the {wl.name} workload (positions {pos[0]}..{pos[-1]}), "
-                      f"indexer score + top-k, {dt:.1f} s wall on {threads} threads"}
+            "sample": f"{what} of the {wl.name} workload, indexer score + top-k, "
+                      f"{dt:.1f} s wall on {threads} threads"}
+
+
+def measured_ceilings():
+    """Practical ceilings on this GPU, for context beside the datasheet peaks:
+    a library bf16 GEMM (8192^3, entries N(0,1)/8 like the indexer inputs) and
+    a 4 GiB device-to-device copy.  Both run after the timed region."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    n = 8192
+    a = (torch.randn(n, n, device="cuda", generator=g) / 8).to(torch.bfloat16)
+    b = (torch.randn(n, n, device="cuda", generator=g) / 8).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2 * n ** 3 * reps / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2 * src.numel() * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_8192_TFLOPs": round(gemm, 1), "bf16_gemm_frac_of_peak": round(gemm / PEAK_BF16_TFLOPS, 4),
+            "copy_4GiB_GBps": round(copy, 1), "copy_frac_of_peak": round(copy / PEAK_HBM_GBS, 4)}
 
 
 def main():
@@ -91,6 +148,8 @@ def main():
     ap.add_argument("--workload", default="prefill200k", choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-allf", action="store_true", help="skip the all-F comparison pass")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the library GEMM / device copy ceiling measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (reference for HBM counters)")
     args = ap.parse_args()
@@ -154,18 +213,30 @@ def main():
     idx_mean = float(np.mean(idx_ms))
     value = n_q_total / (idx_mean / 1e3)
 
-    # roofline of the dominant kernel (indexer score, MFMA-bound in prefill)
+    # roofline of the dominant kernel: the indexer score, MFMA-bound for a
+    # prefill chunk, HBM-bound for decode (one query row per sequence)
     pairs = sum(pairs_in_chunk(q0, tq) for (q0, tq, _, _, _, _) in plans) * wl.B
     flops_per_pair = 2 * wl.H_I * wl.D_I
     n_f = sum(pattern)
     score_s = float(np.mean(score_ms)) / 1e3
-    achieved = pairs * flops_per_pair * n_f / score_s / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": score_traffic(wl),
-                "kernel": "score_prefill_kernel<64,128,bf16>",
-                "launches_per_step": nchunk * n_f,
-                "avg_launch_ms": round(float(np.mean(score_ms)) / (nchunk * n_f), 4)}
+    kdt = "fp8" if wl.key_fp8 else "bf16"
+    if wl.T_q > 1:
+        achieved = pairs * flops_per_pair * n_f / score_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": score_traffic(wl),
+                    "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
+    else:
+        # keys (+ fp8 scale) read once per sequence, queries and weights, score row written
+        key_b = wl.D_I * (1 if wl.key_fp8 else 2) + (4 if wl.key_fp8 else 0)
+        sc_bytes = wl.B * (wl.T_kv * (key_b + 4) + wl.H_I * (wl.D_I * 2 + 4)) * n_f
+        achieved = sc_bytes / score_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": score_traffic(wl),
+                    "kernel": f"score_splitkey_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
+    roofline["launches_per_step"] = nchunk * n_f
+    roofline["avg_launch_ms"] = round(float(np.mean(score_ms)) / (nchunk * n_f), 4)
     # select: HBM-bound; algorithmic bytes = read each causal score once + write k indices
     sel_bytes = (pairs * 4 + n_q_total * wl.top_k * 4) * n_f
     sel_gbs = sel_bytes / (float(np.mean(select_ms)) / 1e3) / 1e9
@@ -193,6 +264,10 @@ def main():
         extra["indexer_share_allF"] = round(idx_f / allf_ms, 3)
         extra["indexer_share_fsss"] = round(idx_mean / float(np.mean(step_ms)), 3)
         log(f"[bench] all-F pass: {allf_ms:.1f} ms")
+
+    if not args.no_ceilings:
+        extra["measured_ceilings"] = measured_ceilings()
+        log(f"[bench] ceilings: {extra['measured_ceilings']}")
 
     cpu = None
     if not args.no_cpu:

@@ -85,7 +85,9 @@ extern "C" {
  * Alignment: q, k, w base 16 bytes; q and k strides multiples of 16 bytes;
  * w strides multiples of 4 floats; k_scale 4 bytes.
  * Envelope: H_I in {4, 8, 16, 32, 64}; D_I in {64, 128}; 1 <= top_k <= 2048;
- * T_kv < 2^31.  The fp8 scale of every key must be positive (it is applied
+ * (512 / H_I) * lcsi_score_ld(T_kv) * 4 < 2^31 (the score rows one
+ * workgroup writes stay below 2 GiB: T_kv < 2^22 for H_I = 4, < 2^26 for
+ * H_I = 64), else LCSI_EUNSUPPORTED.  The fp8 scale of every key must be positive (it is applied
  * after the ReLU); NaN inputs are outside the contract. */
 typedef struct lcsi_indexer {
     int32_t B, T_q, T_kv, H_I, D_I, top_k, key_dtype, reserved;

@@ -26,7 +26,9 @@
 //             reads; B = the lane's own 8 p values packed to bf16 -- P never
 //             leaves registers; O^T's layout keeps one head per lane,
 //             matching the softmax state.
-// Each wave owns 16 heads and DV/NDS output dims (NDS = 4 / head groups).
+// Each wave owns 16 heads and DV/NDS output dims; a workgroup has NWH head
+// groups x NDS dim slices = 4 waves for up to 32 heads, 8 waves for 64 heads
+// (so every variant keeps two waves per SIMD resident).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -79,8 +81,8 @@ __device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *lds)
 #endif
 }
 
-template <int DQK, int DV, int NDS, bool SHARED>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
+template <int DQK, int DV, int NWH, int NDS, bool SHARED>
+__global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnArgs a)
 {
     // Row-major KV tile in LDS: each row holds the K row (DQK bf16) and, when
     // V is a separate tensor, the V row after it, plus one 16-byte pad slot.
@@ -92,11 +94,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     constexpr int NDMA = (TK * RS + 63) / 64;         // 1 KB direct loads per tile
     constexpr int BUFB = NDMA * 1024;                 // bytes per tile buffer
     constexpr int QSTEPS = DQK / 32;
-    constexpr int NWH = 4 / NDS;                      // head groups of 16
+    constexpr int NW = NWH * NDS;                     // waves per workgroup
     constexpr int DVW = DV / NDS;                     // output dims per wave
     constexpr int NDT = DVW / 16;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t kv[2][BUFB];
+    // Two separately declared buffers, each named at compile time in the
+    // unrolled tile loop below: the compiler can then tell that the reads of
+    // one buffer do not depend on the direct loads still filling the other,
+    // and lets them overlap (with one array indexed by a run-time buffer
+    // number it waits for every outstanding direct load before each LDS read).
+    __shared__ __attribute__((aligned(1024))) uint8_t kv0[BUFB];
+    __shared__ __attribute__((aligned(1024))) uint8_t kv1[BUFB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
@@ -133,50 +141,47 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     };
     auto usable = [&](int32_t v) -> int32_t { return (v >= 0 && v <= p && v < a.T_kv) ? v : -1; };
     // ---- gather: direct global->LDS loads of one tile (wave w issues loads
-    // w, w+4, ...; lane l of load m fills 16-byte slot 64m + l, which is
+    // w, w+NW, ...; lane l of load m fills 16-byte slot 64m + l, which is
     // chunk c of tile row r).  Unusable indices read row 0 instead (finite
     // data; their keys are masked), pad slots and slots past the tile
     // re-read the row's first chunk.
-    auto gather = [&](int32_t keys, int buf) {
+    auto gather = [&](int32_t keys, uint8_t *dst) {
 #pragma unroll
-        for (int m = wave; m < NDMA; m += 4) {
+        for (int m = wave; m < NDMA; m += NW) {
             const int slot = 64 * m + lane;
             const int row = slot / RS, c = slot - row * RS;
             const int32_t key = __shfl(keys, row < TK ? row : 0);
             const int64_t kr = (row < TK && key >= 0) ? key : 0;
             const uint16_t *src = c < NCK ? kbase + kr * a.k_st + 8 * c
                                  : (c < NCK + NCV ? vbase + kr * a.v_st + 8 * (c - NCK) : kbase + kr * a.k_st);
-            load_to_lds16(src, kv[buf] + 1024 * m);
+            load_to_lds16(src, dst + 1024 * m);
         }
     };
 
     const int32_t keys0 = usable(raw_idx(0));
     int32_t raw_next = raw_idx(1);
-    gather(keys0, 0);
+    gather(keys0, kv0);
     uint32_t vmask = (uint32_t)__ballot(keys0 >= 0);  // bit r: tile row r usable
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int it = 0; it < ntile; ++it) {
-        const int buf = it & 1;
+    // tile `it` computes from `tb` while tile it+1 is gathered into `nb`
+    auto step = [&](int it, const uint8_t *tb, uint8_t *nb) {
         const int32_t keys_next = usable(raw_next);
         raw_next = raw_idx(it + 2);
-        if (it + 1 < ntile) gather(keys_next, buf ^ 1);
+        if (it + 1 < ntile) gather(keys_next, nb);
         const uint32_t vcur = (vmask >> (8 * g)) & 0xFFu;  // this lane's keys 8g .. 8g+7
         const bool any = vmask != 0;
         if (any) {
-            const uint8_t *tb = kv[buf];
             // ---- S^T = K Q^T for 32 keys (two 16-key halves)
-            f32x4 sacc[2];
+            // (the two halves are independent MFMA chains, interleaved)
+            f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+            const uint8_t *kp = tb + (8 * (l16 >> 2) + (l16 & 3)) * ROWB + 16 * g;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int krow = 8 * (l16 >> 2) + 4 * hf + (l16 & 3);
-                const uint8_t *kp = tb + krow * ROWB + 16 * g;
-                f32x4 acc{0, 0, 0, 0};
+            for (int s = 0; s < QSTEPS; ++s) {
 #pragma unroll
-                for (int s = 0; s < QSTEPS; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 64 * s)),
-                                                                  qf[s], acc, 0, 0, 0);
-                sacc[hf] = acc;
+                for (int hf = 0; hf < 2; ++hf)
+                    sacc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 4 * hf * ROWB + 64 * s)), qf[s], sacc[hf], 0, 0, 0);
             }
             // ---- online softmax over this lane's keys 8g .. 8g+7 (head l16)
             float sv[8];
@@ -222,6 +227,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the other buffer have landed
         __syncthreads();
         vmask = (uint32_t)__ballot(keys_next >= 0);
+    };
+    for (int it = 0; it < ntile; it += 2) {
+        step(it, kv0, kv1);
+        if (it + 1 >= ntile) break;
+        step(it + 1, kv1, kv0);
     }
 
     float l_tot = l_run;
@@ -249,34 +259,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     }
 }
 
-// Combine the per-split partial results of one query row:
+// Combine the per-split partial results of one (query row, head):
 // O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s.
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a)
+// One workgroup per (head, row); thread i owns output dims 4i .. 4i+3.
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 {
-    const int64_t row = blockIdx.x;  // b * T_q + t
+    const int h = blockIdx.x;
+    const int64_t row = blockIdx.y;  // b * T_q + t
     const int b = (int)(row / a.T_q), t = (int)(row % a.T_q);
-    const int nq = a.DV / 4;
-    for (int item = threadIdx.x; item < a.H * nq; item += 256) {
-        const int h = item / nq, d = (item % nq) * 4;
-        float M = -__builtin_inff();
-        for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[((row * a.splits + s) * a.H + h) * 2]);
-        f32x4 o{0, 0, 0, 0};
-        float L = 0.f;
-        if (M != -__builtin_inff()) {
-            for (int s = 0; s < a.splits; ++s) {
-                const int64_t r = (row * a.splits + s) * a.H + h;
-                const float ms = a.part_ml[r * 2];
-                if (ms == -__builtin_inff()) continue;
-                const float f = __builtin_amdgcn_exp2f(ms - M);
-                L += a.part_ml[r * 2 + 1] * f;
-                o += *reinterpret_cast<const f32x4 *>(a.part_o + r * a.DV + d) * f;
-            }
+    const int d = 4 * threadIdx.x;
+    if (d >= a.DV) return;
+    float M = -__builtin_inff();
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[((row * a.splits + s) * a.H + h) * 2]);
+    f32x4 o{0, 0, 0, 0};
+    float L = 0.f;
+    if (M != -__builtin_inff()) {
+        for (int s = 0; s < a.splits; ++s) {
+            const int64_t r = (row * a.splits + s) * a.H + h;
+            const float ms = a.part_ml[r * 2];
+            if (ms == -__builtin_inff()) continue;
+            const float f = __builtin_amdgcn_exp2f(ms - M);
+            L += a.part_ml[r * 2 + 1] * f;
+            o += *reinterpret_cast<const f32x4 *>(a.part_o + r * a.DV + d) * f;
         }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        o *= inv;
-        uint16_t *op = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + d;
-        *reinterpret_cast<u32x2 *>(op) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    o *= inv;
+    uint16_t *op = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + d;
+    *reinterpret_cast<u32x2 *>(op) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
 }
 
 template <int DQK, int DV, bool SHARED>
@@ -285,14 +295,14 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
     dim3 grid(a.splits, a.T_q, a.B);
     const int nwh = (a.H + 15) / 16;
     if (nwh == 1)
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 4, SHARED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 4, SHARED>), grid, dim3(256), 0, st, a);
     else if (nwh == 2)
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, SHARED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, SHARED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 4, 2, SHARED>), grid, dim3(512), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.T_q), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.B * a.T_q), dim3(128), 0, st, a);
     return hipGetLastError();
 }
 

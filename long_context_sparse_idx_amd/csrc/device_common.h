@@ -82,6 +82,24 @@ __device__ __forceinline__ float sum_lane_halves(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 32-bit store through a buffer resource over [base, base + bytes): a lane
+// whose byte offset is not below `bytes` has its store dropped by the
+// hardware's range check, so per-lane masking needs no branch (and the
+// compiler can count outstanding memory operations exactly).  base and
+// bytes must be wave-uniform; bytes < 2^31.
+__device__ __forceinline__ void store_b32_ranged(float *base, uint32_t bytes, uint32_t off, float v)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000),
+                                          (int)off, 0, 0);
+#else
+    (void)base;
+    (void)bytes;
+    (void)off;
+    (void)v;
+#endif
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll

@@ -136,31 +136,37 @@ __device__ __forceinline__ Part<H> epi_reduce(const f32x16 &acc0, const f32x16 &
     return p;
 }
 
+// Rows of the score matrix a workgroup writes: rows t_lo .. t_lo + n - 1
+// starting at `base`, row stride ld floats.  Stores past them (query rows
+// beyond T_q) and masked lanes are dropped by the buffer range check.
+struct RowSpan {
+    float *base;
+    uint32_t bytes;
+    int64_t ld;
+    int t_lo;
+};
+
 template <int H>
-__device__ __forceinline__ void epi_store(const Part<H> &p, float *Sb, int64_t ld, int T_q, int tq0, int key, int lane)
+__device__ __forceinline__ void epi_store(const Part<H> &p, const RowSpan &rs, bool key_ok, int tq0, int key, int lane)
 {
     const int g = lane >> 5;
+    auto put = [&](bool mine, int t, float v) {
+        const uint32_t off = mine ? (uint32_t)(((int64_t)(t - rs.t_lo) * rs.ld + key) * 4) : rs.bytes;
+        store_b32_ranged(rs.base, rs.bytes, off, v);
+    };
     if constexpr (H >= 8) {
         constexpr int QPW = 64 / H;
         if constexpr (QPW == 1) {
-            if (g == 0 && tq0 < T_q) Sb[(int64_t)tq0 * ld + key] = p.v[0];
+            put(key_ok && g == 0, tq0, p.v[0]);
         } else {
 #pragma unroll
-            for (int q = 0; q < QPW; ++q) {
-                const bool mine = (q < QPW / 2) == (g == 0);
-                const int t = tq0 + q;
-                if (mine && t < T_q) Sb[(int64_t)t * ld + key] = p.v[q];
-            }
+            for (int q = 0; q < QPW; ++q) put(key_ok && (q < QPW / 2) == (g == 0), tq0 + q, p.v[q]);
         }
     } else {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = tq0 + rt * 8 + 2 * j + g;
-                if (t < T_q) Sb[(int64_t)t * ld + key] = p.v[rt * 4 + j];
-            }
-        }
+            for (int j = 0; j < 4; ++j) put(key_ok, tq0 + rt * 8 + 2 * j + g, p.v[rt * 4 + j]);
     }
 }
 
@@ -253,6 +259,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     };
 
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
+    const RowSpan rs{Sb + (int64_t)t0 * a.ld, (uint32_t)((t_end - t0) * a.ld * 4), a.ld, t0};
     // Software pipeline inside each wave: while the MFMAs of block j run, the
     // VALU reduces block j-1 (its accumulators wait in pa0/pa1), so the
     // matrix and vector units overlap within one wave as well as across the
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
-            if (pkey >= 0) epi_store<H>(pp, Sb, a.ld, a.T_q, tq0, pkey, lane);
+            epi_store<H>(pp, rs, pkey >= 0, tq0, pkey, lane);
             pa0 = acc0;
             pa1 = acc1;
             pkey = it * KT + cb * 32 + l32;
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         if (it + 1 < ntiles) stash(buf ^ 1);
         __syncthreads();
     }
-    if (pkey >= 0) epi_store<H>(epi_reduce<H>(pa0, pa1, rows.wl, pks), Sb, a.ld, a.T_q, tq0, pkey, lane);
+    epi_store<H>(epi_reduce<H>(pa0, pa1, rows.wl, pks), rs, pkey >= 0, tq0, pkey, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -322,6 +329,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     rows.load(a, b, tq0, lane);
     const uint8_t *kb = a.k + b * a.k_sb;
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
+    const RowSpan rs{Sb + (int64_t)tq0 * a.ld, (uint32_t)((min(a.T_q, tq0 + QPW) - tq0) * a.ld * 4), a.ld, tq0};
 
     u32x4 cur[NLD], nxt[NLD];
     float cs = 1.f, ns = 1.f;
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
         f32x16 acc0, acc1;
         mfma_block<D>(rows.qa, bk, acc0, acc1);
         const int64_t key = key_lo + (int64_t)blk * 32 + l32;
-        epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), Sb, a.ld, a.T_q, tq0, (int)key, lane);
+        epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), rs, true, tq0, (int)key, lane);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) cur[i] = nxt[i];
         cs = ns;

@@ -53,6 +53,7 @@ struct Shared {
     int wtie[NW];
     uint32_t kth;
     int rem;
+    int ge;
     uint32_t kmin, kmax;
 };
 
@@ -101,12 +102,14 @@ struct GlobalRow {
 // range kmax - kmin, so the first 256 bins span the keys actually present
 // (scores of one row share sign and exponent bits, and a digit over those
 // bits would put nearly every key into one or two bins).
-// resolve < 32 stops once that many offset bits from the top are fixed:
-// sh.kth is then kmin + the offset prefix with the lower bits cleared -- a
-// lower bound of the rank-th key that at least `rank` keys reach (used for
-// the sampled threshold, where only a bound is needed).
+// resolve < 32 stops once that many offset bits from the top are fixed and
+// at most max_ge keys lie at or above the current bin: sh.kth is then kmin +
+// the offset prefix with the lower bits cleared -- a lower bound of the
+// rank-th key that at least `rank` and at most max_ge keys reach (used for
+// the sampled threshold, where only a bound is needed; max_ge keeps the
+// bound tight when the keys span a wide range, e.g. scores of both signs).
 template <class Src>
-__device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 32)
+__device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 32, int max_ge = 0x7FFFFFFF)
 {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (tid == 0) {
@@ -178,6 +181,7 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 3
                     if (acc + (int)c[e] >= rem) {
                         sh.kth = prefix | ((uint32_t)(4 * lane + e) << shift);
                         sh.rem = rem - acc;
+                        sh.ge = (rank - rem) + acc + (int)c[e];  // keys at or above this bin
                         break;
                     }
                     acc += (int)c[e];
@@ -188,7 +192,7 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 3
         prefix = sh.kth;
         rem = sh.rem;
         mask |= dmask << shift;
-        if (shift == 0 || msb - shift + 1 >= resolve) break;
+        if (shift == 0 || (msb - shift + 1 >= resolve && sh.ge <= max_ge)) break;
         hi = shift - 1;
     }
     __syncthreads();  // every thread has read sh.kth / sh.rem above
@@ -331,8 +335,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
     r = r < 1 ? 1 : (r > NSAMP ? NSAMP : r);
     // a lower bound of the r-th sampled key, resolved to 1/256 of the
-    // samples' key range, is precise enough for a threshold
-    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r, 8);
+    // samples' key range, is precise enough for a threshold -- unless its
+    // bin holds so many samples that the expected pass count would crowd
+    // the candidate lists (7/8 of their capacity); then refine further
+    const int64_t cap = (int64_t)NW * CAPW * 7 / 8 * NSAMP / n;
+    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r, 8, (int)(cap > r ? cap : r));
     const uint32_t tau = sh.kth;
     __syncthreads();  // every thread has read tau before the lists overwrite the samples
 
