@@ -87,7 +87,8 @@ extern "C" {
  * Envelope: H_I in {4, 8, 16, 32, 64}; D_I in {64, 128}; 1 <= top_k <= 2048;
  * (512 / H_I) * lcsi_score_ld(T_kv) * 4 < 2^31 (the score rows one
  * workgroup writes stay below 2 GiB: T_kv < 2^22 for H_I = 4, < 2^26 for
- * H_I = 64), else LCSI_EUNSUPPORTED.  The fp8 scale of every key must be positive (it is applied
+ * H_I = 64), and a key row stride below 16 MiB, else LCSI_EUNSUPPORTED.
+ * The fp8 scale of every key must be positive (it is applied
  * after the ReLU); NaN inputs are outside the contract. */
 typedef struct lcsi_indexer {
     int32_t B, T_q, T_kv, H_I, D_I, top_k, key_dtype, reserved;

@@ -44,6 +44,8 @@ int check_indexer(const lcsi_indexer *a, bool preset)
     if (!(a->D_I == 64 || a->D_I == 128)) return LCSI_EUNSUPPORTED;
     // the score rows of one workgroup (512/H rows) are addressed with 32-bit offsets
     if ((int64_t)(512 / H) * score_ld(a->T_kv) * 4 >= ((int64_t)1 << 31)) return LCSI_EUNSUPPORTED;
+    // a 128-key tile of keys is addressed with 32-bit offsets
+    if (a->k_st * (fp8 ? 1 : 2) * 128 >= ((int64_t)1 << 31)) return LCSI_EUNSUPPORTED;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 16)) return LCSI_EALIGN;
     if (!mult(a->q_sb, 8) || !mult(a->q_st, 8) || !mult(a->q_sh, 8)) return LCSI_EALIGN;
     const int64_t kel = fp8 ? 16 : 8;  // elements per 16 bytes

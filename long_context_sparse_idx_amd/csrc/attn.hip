@@ -68,19 +68,6 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint8_t *p)
 #endif
 }
 
-// Direct global->LDS load (global_load_lds_dwordx4): every lane loads 16
-// bytes from its own address; lane l's bytes land at lds + 16*l (lds is
-// wave-uniform).  Device pass only, as above.
-__device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *lds)
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-#else
-    (void)src;
-    (void)lds;
-#endif
-}
-
 template <int DQK, int DV, int NWH, int NDS, bool SHARED>
 __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnArgs a)
 {

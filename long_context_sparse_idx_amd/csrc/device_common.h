@@ -100,6 +100,62 @@ __device__ __forceinline__ void store_b32_ranged(float *base, uint32_t bytes, ui
 #endif
 }
 
+// Direct global->LDS load (global_load_lds_dwordx4): every lane loads 16
+// bytes from its own address; lane l's bytes land at lds + 16*l (lds is
+// wave-uniform).  The builtin is only spelled out for the device pass: in
+// the host pass of the same source an LDS builtin on a computed pointer
+// suppresses the host-side launch stub of the kernel that calls it, and a
+// __device__ function never runs on the host.
+__device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+    (void)src;
+    (void)lds;
+#endif
+}
+
+// Direct buffer->LDS load (buffer_load_dwordx4 ... lds) of 16 bytes per lane
+// from base + off, through a buffer resource of `bytes` bytes: a lane whose
+// 16 bytes lie past the end gets zeros.  Lane l's bytes land at lds + 16*l
+// (base, bytes and lds wave-uniform; bytes < 2^31).  Device pass only, as
+// above.
+__device__ __forceinline__ void buffer_load_to_lds16(const void *base, uint32_t bytes, uint32_t off, uint8_t *lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000),
+        (__attribute__((address_space(3))) void *)lds, 16, (int)off, 0, 0, 0);
+#else
+    (void)base;
+    (void)bytes;
+    (void)off;
+    (void)lds;
+#endif
+}
+
+// Workgroup barrier for LDS hand-offs only: no memory-model fence, so the
+// compiler does not wait for this wave's outstanding global stores or
+// direct-to-LDS loads (the caller waits for what it needs first); the empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt on the vector-memory counter only: wait until at most N vector
+// memory operations of this wave are outstanding (N < 64); LDS and export
+// counters are not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll

@@ -185,11 +185,22 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&qa)[2][KeyGeom<D>::KST
 
 // ---------------------------------------------------------------------------
 // Prefill: one workgroup = 8 waves = 8*64/H consecutive query rows of one
-// sequence, sweeping keys 0 .. p_max in 64-key tiles staged (as bf16) in a
-// double-buffered LDS ring; the next tile is fetched into registers while the
-// current one feeds the MFMAs.  Workgroups are issued heaviest (last rows)
-// first.  All concurrently running workgroups sweep the keys in the same
-// order, so each XCD's L2 serves a key tile to all its workgroups.
+// sequence, sweeping keys 0 .. p_max in tiles staged (as bf16) in a
+// double-buffered LDS ring while the next tile is in flight.  Workgroups are
+// issued heaviest (last rows) first.  All concurrently running workgroups
+// sweep the keys in the same order, so each XCD's L2 serves a key tile to
+// all its workgroups.
+//   bf16 keys: 128-key tiles copied straight from memory into LDS
+//              (global_load_lds, no staging registers), rows padded by one
+//              16-byte slot so the B-fragment reads are free of bank
+//              conflicts; the two buffers are separate LDS arrays named at
+//              compile time (the tile loop is unrolled by two), so reads of
+//              one never wait for the loads filling the other.
+//   fp8 keys:  64-key tiles fetched into registers, widened to bf16 and
+//              written to LDS.
+// Inside each wave the MFMAs of a 32-key block overlap the epilogue of the
+// previous block (software pipeline; the accumulators of block j-1 wait in
+// pa0/pa1 while block j runs).
 // ---------------------------------------------------------------------------
 template <int H, int D, bool FP8>
 __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(ScoreArgs a)
@@ -198,14 +209,12 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     constexpr int QPW = 64 / H;
     constexpr int QPB = WAVES_PREFILL * QPW;
     constexpr int NT = WAVES_PREFILL * 64;
-    constexpr int KT = 64;  // keys per LDS tile (two 32-key MFMA blocks)
-    // 16-byte chunks of one tile as stored in LDS (bf16) and as read from HBM
-    constexpr int SRC_CHUNK_KEY = FP8 ? D / 16 : D / 8;   // per key
-    constexpr int SRC_CHUNKS = KT * SRC_CHUNK_KEY;
-    constexpr int CPT = (SRC_CHUNKS + NT - 1) / NT;
+    constexpr int KT = (FP8 || H < 16) ? 64 : 128;  // keys per LDS tile
+    constexpr int SPB = H >= 8 ? QPW : 8;  // score stores per 32-key block and wave
 
-    __shared__ __attribute__((aligned(16))) uint8_t sk[2][KT * G::ROWB];
-    __shared__ float ssc[2][KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t sk0[KT * G::ROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sk1[KT * G::ROWB];
+    __shared__ float ssc[2][FP8 ? KT : 1];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
     const int b = blockIdx.y;
@@ -219,87 +228,129 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     const int tq0 = t0 + wave * QPW;
     rows.load(a, b, tq0, lane);
 
-    u32x4 pf[CPT];
-    float pfs = 1.f;
-    auto fetch = [&](int tile) {
-        const int64_t key0 = (int64_t)tile * KT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
-            const int64_t key = key0 + kk;
-            pf[i] = u32x4{0, 0, 0, 0};
-            if (c < SRC_CHUNKS && key < n_keys) pf[i] = ld16(kb + key * a.k_st + part * 16);
-        }
-        if constexpr (FP8) {
-            const int64_t key = key0 + tid;
-            pfs = (tid < KT && key < n_keys) ? a.k_scale[b * a.ks_sb + key] : 1.f;
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            if (c >= SRC_CHUNKS) break;
-            const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
-            uint8_t *dst = sk[buf] + kk * G::ROWB;
-            if constexpr (FP8) {
-                // 16 fp8 bytes -> 16 bf16 (32 bytes)
-                u32x2 lo0 = fp8x4_to_bf16x4(pf[i].x), lo1 = fp8x4_to_bf16x4(pf[i].y);
-                u32x2 hi0 = fp8x4_to_bf16x4(pf[i].z), hi1 = fp8x4_to_bf16x4(pf[i].w);
-                st16(dst + part * 32, u32x4{lo0.x, lo0.y, lo1.x, lo1.y});
-                st16(dst + part * 32 + 16, u32x4{hi0.x, hi0.y, hi1.x, hi1.y});
-            } else {
-                st16(dst + part * 16, pf[i]);
-            }
-        }
-        if constexpr (FP8) {
-            if (tid < KT) ssc[buf][tid] = pfs;
-        }
-    };
-
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
     const RowSpan rs{Sb + (int64_t)t0 * a.ld, (uint32_t)((t_end - t0) * a.ld * 4), a.ld, t0};
-    // Software pipeline inside each wave: while the MFMAs of block j run, the
-    // VALU reduces block j-1 (its accumulators wait in pa0/pa1), so the
-    // matrix and vector units overlap within one wave as well as across the
-    // two waves of a SIMD.
     f32x16 pa0 = f32x16{0}, pa1 = f32x16{0};
     int pkey = -1;
     float pks = 1.f;
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < ntiles) fetch(it + 1);
+
+    // One 32-key block of the tile at `tb`: B fragments from LDS, 16 MFMAs,
+    // interleaved with the epilogue (ReLU * w, head reduction, store) of the
+    // previous block.
+    auto block = [&](const uint8_t *tb, int cb, float ksc, int key) {
+        const uint8_t *src = tb + (cb * 32 + l32) * G::ROWB + g * G::HALF * 2;
+        bf16x8 bk[G::KSTEPS];
 #pragma unroll
-        for (int cb = 0; cb < KT / 32; ++cb) {
-            const uint8_t *src = sk[buf] + (cb * 32 + l32) * G::ROWB + g * G::HALF * 2;
-            bf16x8 bk[G::KSTEPS];
+        for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
+        f32x16 acc0, acc1;
+        mfma_block<D>(rows.qa, bk, acc0, acc1);
+        const Part<H> pp = epi_reduce<H>(pa0, pa1, rows.wl, pks);
+        // shape: the B-fragment reads, then MFMAs interleaved with VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, G::KSTEPS, 0);
 #pragma unroll
-            for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
-            const float ksc = FP8 ? ssc[buf][cb * 32 + l32] : 1.f;
-            f32x16 acc0, acc1;
-            mfma_block<D>(rows.qa, bk, acc0, acc1);
-            const Part<H> pp = epi_reduce<H>(pa0, pa1, rows.wl, pks);
-            // shape: the B-fragment reads, then MFMAs interleaved with VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, G::KSTEPS, 0);
-#pragma unroll
-            for (int i = 0; i < 2 * G::KSTEPS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
-            epi_store<H>(pp, rs, pkey >= 0, tq0, pkey, lane);
-            pa0 = acc0;
-            pa1 = acc1;
-            pkey = it * KT + cb * 32 + l32;
-            pks = ksc;
+        for (int i = 0; i < 2 * G::KSTEPS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        if (it + 1 < ntiles) stash(buf ^ 1);
+        // (columns past the last key are not stored: a tile may reach
+        // beyond the row stride)
+        epi_store<H>(pp, rs, pkey >= 0 && pkey < n_keys, tq0, pkey, lane);
+        pa0 = acc0;
+        pa1 = acc1;
+        pkey = key;
+        pks = ksc;
+    };
+
+    if constexpr (!FP8) {
+        constexpr int RS = G::ROWB / 16;     // 16-byte slots per LDS row (D/8 + 1 pad)
+        constexpr int NDMA = KT * RS / 64;   // 1 KB direct loads per tile
+        constexpr int MPW = (NDMA + WAVES_PREFILL - 1) / WAVES_PREFILL;
+        static_assert(KT * RS % 64 == 0, "tile must fill whole direct loads");
+        // lane l of load m fills slot 64m + l = chunk c of tile row r (pad
+        // slots re-read chunk 0); rows past the last key read as zeros
+        uint32_t goff[MPW];
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int slot = 64 * (wave + WAVES_PREFILL * i) + lane;
+            const int row = slot / RS, c = slot - row * RS;
+            goff[i] = (uint32_t)(row * a.k_st + (c < RS - 1 ? 16 * c : 0));
+        }
+        auto gather = [&](int tile, uint8_t *dst) {
+            const int64_t key0 = (int64_t)tile * KT;
+            const uint8_t *tbase = kb + key0 * a.k_st;
+            const uint32_t bytes = (uint32_t)(min<int64_t>(n_keys - key0, KT) * a.k_st);
+#pragma unroll
+            for (int i = 0; i < MPW; ++i) {
+                const int m = wave + WAVES_PREFILL * i;
+                if (m < NDMA) buffer_load_to_lds16(tbase, bytes, goff[i], dst + 1024 * m);
+            }
+        };
+        auto step = [&](int it, const uint8_t *tb, uint8_t *nb) {
+            if (it + 1 < ntiles) gather(it + 1, nb);
+#pragma unroll
+            for (int cb = 0; cb < KT / 32; ++cb) block(tb, cb, 1.f, it * KT + cb * 32 + l32);
+            // this wave's loads into nb have landed (only the score stores
+            // issued after them may still be in flight), then all waves' have
+            wait_vmcnt<(KT / 32) * SPB>();
+            lds_barrier();
+        };
+        gather(0, sk0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        for (int it = 0; it < ntiles; it += 2) {
+            step(it, sk0, sk1);
+            if (it + 1 >= ntiles) break;
+            step(it + 1, sk1, sk0);
+        }
+    } else {
+        // 16-byte chunks of one tile as read from memory: D/16 per key
+        constexpr int SRC_CHUNK_KEY = D / 16;
+        constexpr int SRC_CHUNKS = KT * SRC_CHUNK_KEY;
+        constexpr int CPT = (SRC_CHUNKS + NT - 1) / NT;
+        u32x4 pf[CPT];
+        float pfs = 1.f;
+        auto fetch = [&](int tile) {
+            const int64_t key0 = (int64_t)tile * KT;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = tid + i * NT;
+                const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
+                const int64_t key = key0 + kk;
+                pf[i] = u32x4{0, 0, 0, 0};
+                if (c < SRC_CHUNKS && key < n_keys) pf[i] = ld16(kb + key * a.k_st + part * 16);
+            }
+            const int64_t key = key0 + tid;
+            pfs = (tid < KT && key < n_keys) ? a.k_scale[b * a.ks_sb + key] : 1.f;
+        };
+        auto stash = [&](uint8_t *dst, int buf) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = tid + i * NT;
+                if (c >= SRC_CHUNKS) break;
+                const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
+                uint8_t *row = dst + kk * G::ROWB;
+                // 16 fp8 bytes -> 16 bf16 (32 bytes)
+                u32x2 lo0 = fp8x4_to_bf16x4(pf[i].x), lo1 = fp8x4_to_bf16x4(pf[i].y);
+                u32x2 hi0 = fp8x4_to_bf16x4(pf[i].z), hi1 = fp8x4_to_bf16x4(pf[i].w);
+                st16(row + part * 32, u32x4{lo0.x, lo0.y, lo1.x, lo1.y});
+                st16(row + part * 32 + 16, u32x4{hi0.x, hi0.y, hi1.x, hi1.y});
+            }
+            if (tid < KT) ssc[buf][tid] = pfs;
+        };
+        fetch(0);
+        stash(sk0, 0);
         __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+            const int buf = it & 1;
+            if (it + 1 < ntiles) fetch(it + 1);
+#pragma unroll
+            for (int cb = 0; cb < KT / 32; ++cb)
+                block(buf ? sk1 : sk0, cb, ssc[buf][cb * 32 + l32], it * KT + cb * 32 + l32);
+            if (it + 1 < ntiles) stash(buf ? sk0 : sk1, buf ^ 1);
+            __syncthreads();
+        }
     }
-    epi_store<H>(epi_reduce<H>(pa0, pa1, rows.wl, pks), rs, pkey >= 0, tq0, pkey, lane);
+    epi_store<H>(epi_reduce<H>(pa0, pa1, rows.wl, pks), rs, pkey >= 0 && pkey < n_keys, tq0, pkey, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,7 +413,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
         f32x16 acc0, acc1;
         mfma_block<D>(rows.qa, bk, acc0, acc1);
         const int64_t key = key_lo + (int64_t)blk * 32 + l32;
-        epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), rs, true, tq0, (int)key, lane);
+        epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), rs, key < key_hi, tq0, (int)key, lane);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) cur[i] = nxt[i];
         cs = ns;
