@@ -69,7 +69,7 @@ def _load():
         lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_score_select_rows.argtypes = [
-            i32, p, p, p, p, p, i32, i64, i32, i32, i32, p, i64, p, i32]
+            i32, p, p, p, i32, p, p, p, i32, i64, i32, i32, i32, p, i64, p, i32]
         lib.oracle_score_select_rows.restype = i32
         lib.oracle_select_rows.argtypes = [i32, p, i64, p, i32, p, i32]
         lib.oracle_select_rows.restype = i32
@@ -112,10 +112,11 @@ def double_to_bf16(x: float) -> int:
 # ------------------------------------------------------------ score / select
 
 def score_select(q_rows, w_rows, keys, pos, top_k, k_scale=None,
-                 want_scores=True, threads=None):
+                 want_scores=True, threads=None, q_scale=None):
     """Indexer score + top-k for a list of query rows sharing one key array.
 
-    q_rows : uint16 [R, H, D]  (bf16 bit patterns)
+    q_rows : uint16 [R, H, D] (bf16 bit patterns) or uint8 [R, H, D] (fp8
+             e4m3 bytes, then q_scale float32 [R, H] gives each head's scale)
     w_rows : float32 [R, H]
     keys   : uint16 [N, D] (bf16 bits) or uint8 [N, D] (fp8 e4m3 bytes)
     pos    : int64 [R] absolute position p of each row (it sees keys 0..p)
@@ -123,10 +124,13 @@ def score_select(q_rows, w_rows, keys, pos, top_k, k_scale=None,
     Returns (scores float32 [R, max_p+1] or None, idx int32 [R, top_k]).
     Entries of a score row past its p are left at 0.
     """
-    q_rows = _c(q_rows, np.uint16)
+    q_fp8 = np.asarray(q_rows).dtype == np.uint8
+    q_rows = _c(q_rows, np.uint8 if q_fp8 else np.uint16)
+    qs = _c(q_scale, np.float32) if q_fp8 else None
     w_rows = _c(w_rows, np.float32)
     pos = _c(pos, np.int64)
     R, H, D = q_rows.shape
+    assert not q_fp8 or qs.shape == (R, H)
     key_fp8 = keys.dtype == np.uint8
     keys = _c(keys, np.uint8 if key_fp8 else np.uint16)
     assert keys.shape[1] == D and keys.shape[0] > int(pos.max(initial=-1))
@@ -135,7 +139,7 @@ def score_select(q_rows, w_rows, keys, pos, top_k, k_scale=None,
     scores = np.zeros((R, max(n_max, 1)), np.float32) if want_scores else None
     idx = np.empty((R, top_k), np.int32)
     _load().oracle_score_select_rows(
-        R, _ptr(pos), _ptr(q_rows), _ptr(w_rows), _ptr(keys), _ptr(ks),
+        R, _ptr(pos), _ptr(q_rows), _ptr(qs), int(q_fp8), _ptr(w_rows), _ptr(keys), _ptr(ks),
         int(key_fp8), D, H, D, top_k, _ptr(scores),
         scores.shape[1] if want_scores else 0, _ptr(idx),
         threads or default_threads())

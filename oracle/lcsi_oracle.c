@@ -91,14 +91,19 @@ uint16_t oracle_double_to_bf16(double x)
 /* One score row: out[s] for s = 0..n-1 (n = p+1 causal keys).
  * q: bf16 bits [H][D]; w: [H]; keys: [n][D] bf16 bits (key_fp8 = 0) or fp8
  * bytes with a per-key scale (key_fp8 = 1), row stride k_ld elements. */
-void oracle_score_row(const uint16_t *q, const float *w, const void *keys,
+/* Query rows come as bf16, or as fp8 e4m3 with one positive scale per head
+ * (q_scale[h]); either way each element is decoded exactly and an fp8 query
+ * element stands for fp8 value * scale, the same reading as an fp8 key. */
+void oracle_score_row(const void *q, const float *q_scale, int q_fp8,
+                      const float *w, const void *keys,
                       const float *k_scale, int key_fp8, int64_t k_ld, int H,
                       int D, int64_t n, float *out)
 {
     double *qd = malloc(sizeof(double) * (size_t)H * D);
     double *kd = malloc(sizeof(double) * (size_t)D);
     for (int i = 0; i < H * D; i++)
-        qd[i] = oracle_bf16_to_double(q[i]);
+        qd[i] = q_fp8 ? oracle_fp8e4m3_to_double(((const uint8_t *)q)[i]) * (double)q_scale[i / D]
+                      : oracle_bf16_to_double(((const uint16_t *)q)[i]);
     for (int64_t s = 0; s < n; s++) {
         for (int d = 0; d < D; d++) {
             if (key_fp8) {
@@ -224,7 +229,9 @@ void oracle_attn_row(const uint16_t *q, const uint16_t *K, int64_t k_ld,
 typedef struct {
     int n_rows;
     const int64_t *pos;      /* [n_rows] absolute position p of each row */
-    const uint16_t *q_rows;  /* [n_rows][H][D] */
+    const void *q_rows;      /* [n_rows][H][D] bf16 bits, or fp8 bytes */
+    const float *q_scale;    /* [n_rows][H] when q_fp8, else NULL */
+    int q_fp8;
     const float *w_rows;     /* [n_rows][H] */
     const void *keys;        /* [>= max p + 1][k_ld] */
     const float *k_scale;
@@ -260,7 +267,10 @@ static void *score_worker(void *arg)
             break;
         int64_t n = j->pos[r] + 1;
         float *s = j->scores ? j->scores + (int64_t)r * j->s_ld : tmp;
-        oracle_score_row(j->q_rows + (size_t)r * j->H * j->D,
+        const size_t qel = (size_t)r * j->H * j->D;
+        oracle_score_row(j->q_fp8 ? (const void *)((const uint8_t *)j->q_rows + qel)
+                                  : (const void *)((const uint16_t *)j->q_rows + qel),
+                         j->q_fp8 ? j->q_scale + (size_t)r * j->H : NULL, j->q_fp8,
                          j->w_rows + (size_t)r * j->H, j->keys, j->k_scale,
                          j->key_fp8, j->k_ld, j->H, j->D, n, s);
         if (j->idx)
@@ -285,13 +295,14 @@ static void run_threads(void *(*fn)(void *), void *job, int threads)
 /* Score (and optionally select) a list of rows that share one key array.
  * scores may be NULL (then only idx is produced); idx may be NULL. */
 int oracle_score_select_rows(int n_rows, const int64_t *pos,
-                             const uint16_t *q_rows, const float *w_rows,
+                             const void *q_rows, const float *q_scale, int q_fp8,
+                             const float *w_rows,
                              const void *keys, const float *k_scale,
                              int key_fp8, int64_t k_ld, int H, int D, int top_k,
                              float *scores, int64_t s_ld, int32_t *idx,
                              int threads)
 {
-    score_job_t j = {n_rows, pos, q_rows, w_rows, keys, k_scale, key_fp8,
+    score_job_t j = {n_rows, pos, q_rows, q_scale, q_fp8, w_rows, keys, k_scale, key_fp8,
                      k_ld, H, D, top_k, scores, s_ld, idx, 0,
                      PTHREAD_MUTEX_INITIALIZER};
     run_threads(score_worker, &j, threads);

@@ -223,6 +223,32 @@ def test_fp8_keys_equal_bf16_keys_with_same_values():
     assert np.allclose(s3, 3 * s1, rtol=2 ** -23, atol=0)
 
 
+def test_fp8_queries_equal_bf16_queries_with_same_values():
+    """fp8 queries with a per-head scale decode to value * scale: with
+    power-of-two scales that is exactly a bf16 value, so scores must equal the
+    bf16-query scores bit for bit.  Distinct scales per head catch a scale
+    applied to the wrong head (or per row instead of per head)."""
+    rng = np.random.default_rng(16)
+    R, H, D, N = 3, 5, 32, 60
+    k8 = torch.from_numpy(rng.standard_normal((N, D)).astype(np.float32) * 4).to(torch.float8_e4m3fn)
+    kscale = (2.0 ** rng.integers(-5, -1, N)).astype(np.float32)
+    q8 = torch.from_numpy(rng.standard_normal((R, H, D)).astype(np.float32) * 8).to(torch.float8_e4m3fn)
+    qscale = (2.0 ** rng.integers(-6, 0, (R, H))).astype(np.float32)
+    w = rng.uniform(0, 1, (R, H)).astype(np.float32)
+    pos = np.array([7, 33, 59])
+    qval = q8.to(torch.float64).numpy() * qscale[:, :, None]
+    kb = k8.view(torch.uint8).numpy()
+    s8, i8 = oracle.score_select(q8.view(torch.uint8).numpy(), w, kb, pos, 9, k_scale=kscale, q_scale=qscale)
+    sb, ib = oracle.score_select(bf16_bits(qval.astype(np.float32)), w, kb, pos, 9, k_scale=kscale)
+    assert np.array_equal(s8, sb)
+    assert np.array_equal(i8, ib)
+    # the per-head scale acts like a factor on that head's weight (exact for
+    # powers of two, and ReLU commutes with a positive factor)
+    s1, _ = oracle.score_select(q8.view(torch.uint8).numpy(), w * qscale, kb, pos, 9, k_scale=kscale,
+                                q_scale=np.ones((R, H), np.float32))
+    assert np.array_equal(s8, s1)
+
+
 # -------------------------------------------------------------------- select
 
 def rank_definition(row, k):
