@@ -34,6 +34,7 @@ from long_context_sparse_idx_amd import inputs, lcsi  # noqa: E402
 from long_context_sparse_idx_amd.runner import Workload, pairs_in_chunk  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -73,27 +74,33 @@ def cpu_baseline(path: Workload, max_rows: int | None = None):
 
     def rows_of(b, rows):
         r = torch.as_tensor(rows, device=x["q"].device)
-        q = x["q"][b].index_select(0, r).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        return q, x["w"][b].index_select(0, r).cpu().numpy()
+        if wl.q_fp8:
+            q = x["q"][b].index_select(0, r).cpu().numpy()
+            qs = x["q_scale"][b].index_select(0, r).cpu().numpy()
+        else:
+            q = x["q"][b].index_select(0, r).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            qs = None
+        return q, x["w"][b].index_select(0, r).cpu().numpy(), qs
 
     t0 = time.time()
     if wl.n_q > 1:
         R = max_rows or max(8, 4 * threads)
         pos = np.array([wl.q_pos0 + int((i + 0.5) * wl.n_q / R) for i in range(R)], np.int64)
-        q, w = rows_of(0, pos - wl.q_pos0)
+        q, w, qs = rows_of(0, pos - wl.q_pos0)
         keys, ks = seq_arrays(0)
         t0 = time.time()
-        oracle.score_select(q, w, keys, pos, wl.top_k, k_scale=ks, want_scores=False, threads=threads)
+        oracle.score_select(q, w, keys, pos, wl.top_k, k_scale=ks, want_scores=False, threads=threads,
+                            q_scale=qs)
         what = f"{R} evenly spaced rows of sequence 0 (positions {pos[0]}..{pos[-1]})"
     else:
         R = max_rows or min(wl.B, 4)
         dt = 0.0
         for b in range(R):
-            q, w = rows_of(b, [0])
+            q, w, qs = rows_of(b, [0])
             keys, ks = seq_arrays(b)
             t1 = time.time()
             oracle.score_select(q, w, keys, np.array([wl.q_pos0], np.int64), wl.top_k, k_scale=ks,
-                                want_scores=False, threads=threads)
+                                want_scores=False, threads=threads, q_scale=qs)
             dt += time.time() - t1
         t0 = time.time() - dt
         what = f"the new token of sequences 0..{R - 1} (position {wl.q_pos0}), one row per call"
@@ -219,17 +226,19 @@ def main():
     flops_per_pair = 2 * wl.H_I * wl.D_I
     n_f = sum(pattern)
     score_s = float(np.mean(score_ms)) / 1e3
-    kdt = "fp8" if wl.key_fp8 else "bf16"
+    kdt = "fp8xfp8" if wl.q_fp8 else ("fp8" if wl.key_fp8 else "bf16")
+    peak = PEAK_FP8_TFLOPS if wl.q_fp8 else PEAK_BF16_TFLOPS
     if wl.T_q > 1:
         achieved = pairs * flops_per_pair * n_f / score_s / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": score_traffic(wl),
                     "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
     else:
         # keys (+ fp8 scale) read once per sequence, queries and weights, score row written
         key_b = wl.D_I * (1 if wl.key_fp8 else 2) + (4 if wl.key_fp8 else 0)
-        sc_bytes = wl.B * (wl.T_kv * (key_b + 4) + wl.H_I * (wl.D_I * 2 + 4)) * n_f
+        q_b = wl.D_I * (1 if wl.q_fp8 else 2) + (8 if wl.q_fp8 else 4)
+        sc_bytes = wl.B * (wl.T_kv * (key_b + 4) + wl.H_I * q_b) * n_f
         achieved = sc_bytes / score_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -286,7 +295,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not wl.key_fp8 else "bf16 (fp8 e4m3 keys widened exactly)",
+        "dtype": ("fp8 e4m3 (queries and keys)" if wl.q_fp8 else
+                  "bf16 (fp8 e4m3 keys widened exactly)" if wl.key_fp8 else "bf16"),
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.q_pos0 + wl.n_q, "B": wl.B, "chunk": wl.T_q,
                    "pattern": "".join("F" if f else "S" for f in pattern), "H_I": wl.H_I,

@@ -69,6 +69,10 @@ extern "C" {
 #define LCSI_KEY_BF16 0
 #define LCSI_KEY_FP8_E4M3 1  /* OCP E4M3 ("fn": no infinities, max 448) + fp32 per-key scale > 0 */
 
+/* ---------------------------------------------------------- query dtypes */
+#define LCSI_Q_BF16 0
+#define LCSI_Q_FP8_E4M3 1    /* OCP E4M3 + fp32 per-(token, head) scale > 0; needs fp8 keys */
+
 /* ------------------------------------------------------ idx_score_topk flags */
 #define LCSI_SCORES_PRESET 1u /* skip scoring: select from the scores already in score_ws */
 #define LCSI_SCORES_ONLY 2u   /* score only: leave the scores in score_ws, write no indices */
@@ -84,6 +88,12 @@ extern "C" {
  *   w      fp32  [B][T_q][H_I]        strides w_sb, w_st
  * Alignment: q, k, w base 16 bytes; q and k strides multiples of 16 bytes;
  * w strides multiples of 4 floats; k_scale 4 bytes.
+ * fp8 queries (q_dtype = LCSI_Q_FP8_E4M3, keys fp8 too): q holds e4m3 bytes
+ * [B][T_q][H_I][D_I] (strides in bytes), q_scale fp32 [B][T_q][H_I] with
+ * strides qs_sb, qs_st (heads contiguous); a query element stands for its
+ * value times the scale of its (token, head), as a key element does with its
+ * key's scale.  The products then run on fp8 x fp8 MFMA.  With q_dtype =
+ * LCSI_Q_BF16, q_scale is ignored (NULL).
  * Envelope: H_I in {4, 8, 16, 32, 64}; D_I in {64, 128}; 1 <= top_k <= 2048;
  * (512 / H_I) * lcsi_score_ld(T_kv) * 4 < 2^31 (the score rows one
  * workgroup writes stay below 2 GiB: T_kv < 2^22 for H_I = 4, < 2^26 for
@@ -91,7 +101,7 @@ extern "C" {
  * The fp8 scale of every key must be positive (it is applied
  * after the ReLU); NaN inputs are outside the contract. */
 typedef struct lcsi_indexer {
-    int32_t B, T_q, T_kv, H_I, D_I, top_k, key_dtype, reserved;
+    int32_t B, T_q, T_kv, H_I, D_I, top_k, key_dtype, q_dtype;
     int64_t q_pos0;
     const void *q;
     int64_t q_sb, q_st, q_sh;
@@ -101,6 +111,8 @@ typedef struct lcsi_indexer {
     int64_t ks_sb;
     const float *w;
     int64_t w_sb, w_st;
+    const float *q_scale;
+    int64_t qs_sb, qs_st;
 } lcsi_indexer;
 
 /* Main-attention inputs of one layer (every layer, F or S, has its own).

@@ -33,12 +33,15 @@ int check_indexer(const lcsi_indexer *a, bool preset)
     int rc = check_rows(a->B, a->T_q, a->T_kv, a->q_pos0, a->top_k);
     if (rc || preset) return rc;
     if (a->key_dtype != LCSI_KEY_BF16 && a->key_dtype != LCSI_KEY_FP8_E4M3) return LCSI_EINVAL;
+    if (a->q_dtype != LCSI_Q_BF16 && a->q_dtype != LCSI_Q_FP8_E4M3) return LCSI_EINVAL;
     const bool fp8 = a->key_dtype == LCSI_KEY_FP8_E4M3;
-    if (!a->q || !a->k || !a->w || (fp8 && !a->k_scale)) return LCSI_EINVAL;
+    const bool q8 = a->q_dtype == LCSI_Q_FP8_E4M3;
+    if (!a->q || !a->k || !a->w || (fp8 && !a->k_scale) || (q8 && !a->q_scale)) return LCSI_EINVAL;
     if (a->H_I < 1 || a->D_I < 1) return LCSI_EINVAL;
     if (a->q_sb < 0 || a->q_st < 0 || a->q_sh < 0 || a->k_sb < 0 || a->k_st < 0 || a->w_sb < 0 || a->w_st < 0 ||
-        (fp8 && a->ks_sb < 0))
+        (fp8 && a->ks_sb < 0) || (q8 && (a->qs_sb < 0 || a->qs_st < 0)))
         return LCSI_EINVAL;
+    if (q8 && !fp8) return LCSI_EUNSUPPORTED;  // fp8 x fp8 products need fp8 keys
     const int H = a->H_I;
     if (!(H == 4 || H == 8 || H == 16 || H == 32 || H == 64)) return LCSI_EUNSUPPORTED;
     if (!(a->D_I == 64 || a->D_I == 128)) return LCSI_EUNSUPPORTED;
@@ -47,7 +50,9 @@ int check_indexer(const lcsi_indexer *a, bool preset)
     // a 128-key tile of keys is addressed with 32-bit offsets
     if (a->k_st * (fp8 ? 1 : 2) * 128 >= ((int64_t)1 << 31)) return LCSI_EUNSUPPORTED;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 16)) return LCSI_EALIGN;
-    if (!mult(a->q_sb, 8) || !mult(a->q_st, 8) || !mult(a->q_sh, 8)) return LCSI_EALIGN;
+    const int64_t qel = q8 ? 16 : 8;  // query elements per 16 bytes
+    if (!mult(a->q_sb, qel) || !mult(a->q_st, qel) || !mult(a->q_sh, qel)) return LCSI_EALIGN;
+    if (q8 && !aligned(a->q_scale, 4)) return LCSI_EALIGN;
     const int64_t kel = fp8 ? 16 : 8;  // elements per 16 bytes
     if (!mult(a->k_sb, kel) || !mult(a->k_st, kel)) return LCSI_EALIGN;
     if (!mult(a->w_sb, 4) || !mult(a->w_st, 4)) return LCSI_EALIGN;
@@ -136,11 +141,16 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
         sa.H = a->H_I;
         sa.D = a->D_I;
         sa.fp8 = a->key_dtype == LCSI_KEY_FP8_E4M3;
+        sa.q8 = a->q_dtype == LCSI_Q_FP8_E4M3;
         sa.q_pos0 = a->q_pos0;
-        sa.q = (const uint16_t *)a->q;
-        sa.q_sb = a->q_sb;
-        sa.q_st = a->q_st;
-        sa.q_sh = a->q_sh;
+        const int64_t qbytes = sa.q8 ? 1 : 2;
+        sa.q = (const uint8_t *)a->q;
+        sa.q_sb = a->q_sb * qbytes;
+        sa.q_st = a->q_st * qbytes;
+        sa.q_sh = a->q_sh * qbytes;
+        sa.q_scale = a->q_scale;
+        sa.qs_sb = a->qs_sb;
+        sa.qs_st = a->qs_st;
         const int64_t kbytes = sa.fp8 ? 1 : 2;
         sa.k = (const uint8_t *)a->k;
         sa.k_sb = a->k_sb * kbytes;

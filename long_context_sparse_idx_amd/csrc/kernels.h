@@ -9,10 +9,13 @@ namespace lcsi {
 
 struct ScoreArgs {
     int B, T_q, T_kv, H, D;
-    int fp8;
+    int fp8;                  // keys fp8 e4m3 (+ per-key scale)
+    int q8;                   // queries fp8 e4m3 (+ per-(token, head) scale); needs fp8 keys
     int64_t q_pos0;
-    const uint16_t *q;        // bf16, strides in elements
+    const uint8_t *q;         // bf16 or fp8 rows, strides in BYTES
     int64_t q_sb, q_st, q_sh;
+    const float *q_scale;     // fp8 queries only
+    int64_t qs_sb, qs_st;
     const uint8_t *k;         // bf16 or fp8 rows, strides in BYTES
     int64_t k_sb, k_st;
     const float *k_scale;     // fp8 only

@@ -19,6 +19,14 @@
 // to bf16 on load and the per-key scale is applied after the head reduction
 // (max(0, a x) = a max(0, x) for a > 0).
 //
+// fp8 keys and fp8 queries: the products run on v_mfma_f32_32x32x64_f8f6f4
+// (format 0 = E4M3 on both operands, no block scales) at twice the bf16
+// rate; each (token, head) scale is folded into that head's weight and the
+// key scale is applied after the head reduction, as above.  For that
+// instruction a lane holds 32 bytes of row/column (lane % 32), k-slots of
+// group g; the d index behind slot e of step s is g*D/2 + 32*s + e, again
+// the same on both operands.
+//
 // Lane layouts (32x32x16 bf16 MFMA, wave64, g = lane / 32):
 //   A (Q):  lane holds row (lane % 32), 8 consecutive k-slots of group g
 //   B (K):  lane holds column (lane % 32), the same 8 k-slots of group g
@@ -26,6 +34,8 @@
 // The d index behind k-slot e of group g in k-step s is g*D/2 + 8*s + e: both
 // operands use the same map, so the MFMA still sums all D products, and each
 // lane reads one contiguous half of a row (128 B for D = 128).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,12 +46,20 @@ namespace {
 constexpr int WAVES_PREFILL = 8;  // 512 threads: 2 waves per SIMD
 constexpr int WAVES_SPLIT = 4;
 
+// Operand formats: bf16 keys and queries; fp8 keys widened to bf16; fp8
+// keys and fp8 queries on fp8 MFMA.
+enum Fmt { F_BF16 = 0, F_K8 = 1, F_QK8 = 2 };
+
 template <int D>
 struct KeyGeom {
-    static constexpr int KSTEPS = D / 16;     // MFMA k-steps
+    static constexpr int KSTEPS = D / 16;     // bf16 MFMA k-steps
+    static constexpr int KSTEPS8 = D / 64;    // fp8 MFMA k-steps
     static constexpr int HALF = D / 2;        // d-elements per lane group
     static constexpr int ROWB = D * 2 + 16;   // LDS bytes per bf16 key row (+16 B pad)
+    static constexpr int ROWB8 = D + 16;      // LDS bytes per fp8 key row (+16 B pad)
 };
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Q fragments and per-row weights of one wave (64 rows = 64/H queries).
 template <int H, int D>
@@ -57,9 +75,9 @@ struct WaveRows {
             const int row = rt * 32 + l32;
             const int t = tq0 + row / H, h = row % H;
             if (t < a.T_q) {
-                const uint16_t *base = a.q + b * a.q_sb + (int64_t)t * a.q_st + h * a.q_sh + g * KeyGeom<D>::HALF;
+                const uint8_t *base = a.q + b * a.q_sb + (int64_t)t * a.q_st + h * a.q_sh + g * KeyGeom<D>::HALF * 2;
 #pragma unroll
-                for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(ld16(base + 8 * s));
+                for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(ld16(base + 16 * s));
             } else {
 #pragma unroll
                 for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
@@ -73,6 +91,48 @@ struct WaveRows {
         }
     }
 };
+
+// fp8 variant: Q fragments are 32 bytes per k-step; each head's query scale
+// is folded into its weight.
+template <int H, int D>
+struct WaveRows8 {
+    i32x8 qa[2][KeyGeom<D>::KSTEPS8];
+    float wl[2][16];
+
+    __device__ __forceinline__ void load(const ScoreArgs &a, int b, int tq0, int lane)
+    {
+        const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int row = rt * 32 + l32;
+            const int t = tq0 + row / H, h = row % H;
+#pragma unroll
+            for (int s = 0; s < KeyGeom<D>::KSTEPS8; ++s) {
+                u32x4 lo{0, 0, 0, 0}, hi{0, 0, 0, 0};
+                if (t < a.T_q) {
+                    const uint8_t *base = a.q + b * a.q_sb + (int64_t)t * a.q_st + h * a.q_sh + g * KeyGeom<D>::HALF + 32 * s;
+                    lo = ld16(base);
+                    hi = ld16(base + 16);
+                }
+                qa[rt][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = rt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const int tr = tq0 + rr / H, hr = rr % H;
+                wl[rt][r] = tr < a.T_q ? a.w[b * a.w_sb + (int64_t)tr * a.w_st + hr] *
+                                             a.q_scale[b * a.qs_sb + (int64_t)tr * a.qs_st + hr]
+                                       : 0.f;
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ i32x8 lds_ld32(const uint8_t *p)
+{
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(p), hi = *reinterpret_cast<const u32x4 *>(p + 16);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
 
 // Epilogue of one 32-key block: ReLU * weight and the head reduction
 // (epi_reduce, pure register arithmetic), then the store (epi_store).  The
@@ -183,38 +243,55 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&qa)[2][KeyGeom<D>::KST
     }
 }
 
+template <int D>
+__device__ __forceinline__ void mfma_block8(const i32x8 (&qa)[2][KeyGeom<D>::KSTEPS8], const i32x8 (&bk)[KeyGeom<D>::KSTEPS8],
+                                            f32x16 &acc0, f32x16 &acc1)
+{
+    acc0 = f32x16{0};
+    acc1 = f32x16{0};
+#pragma unroll
+    for (int s = 0; s < KeyGeom<D>::KSTEPS8; ++s) {
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][s], bk[s], acc0, 0, 0, 0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][s], bk[s], acc1, 0, 0, 0, 0, 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: one workgroup = 8 waves = 8*64/H consecutive query rows of one
-// sequence, sweeping keys 0 .. p_max in tiles staged (as bf16) in a
-// double-buffered LDS ring while the next tile is in flight.  Workgroups are
-// issued heaviest (last rows) first.  All concurrently running workgroups
-// sweep the keys in the same order, so each XCD's L2 serves a key tile to
-// all its workgroups.
-//   bf16 keys: 128-key tiles copied straight from memory into LDS
-//              (global_load_lds, no staging registers), rows padded by one
-//              16-byte slot so the B-fragment reads are free of bank
-//              conflicts; the two buffers are separate LDS arrays named at
-//              compile time (the tile loop is unrolled by two), so reads of
-//              one never wait for the loads filling the other.
-//   fp8 keys:  64-key tiles fetched into registers, widened to bf16 and
-//              written to LDS.
+// sequence, sweeping keys 0 .. p_max in tiles staged in a double-buffered LDS
+// ring while the next tile is in flight.  Workgroups are issued heaviest
+// (last rows) first.  All concurrently running workgroups sweep the keys in
+// the same order, so each XCD's L2 serves a key tile to all its workgroups.
+//   bf16 keys, and fp8 keys with fp8 queries: 128-key tiles copied straight
+//              from memory into LDS (buffer loads to LDS, no staging
+//              registers), rows padded by one 16-byte slot so the B-fragment
+//              reads are free of bank conflicts (fp8: the tile's key scales
+//              follow the rows); the two buffers are separate LDS arrays
+//              named at compile time (the tile loop is unrolled by two), so
+//              reads of one never wait for the loads filling the other.
+//   fp8 keys with bf16 queries: 64-key tiles fetched into registers,
+//              widened to bf16 and written to LDS.
 // Inside each wave the MFMAs of a 32-key block overlap the epilogue of the
 // previous block (software pipeline; the accumulators of block j-1 wait in
 // pa0/pa1 while block j runs).
 // ---------------------------------------------------------------------------
-template <int H, int D, bool FP8>
+template <int H, int D, int F>
 __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(ScoreArgs a)
 {
     using G = KeyGeom<D>;
+    constexpr bool Q8 = F == F_QK8;
+    constexpr bool DMA = F != F_K8;
     constexpr int QPW = 64 / H;
     constexpr int QPB = WAVES_PREFILL * QPW;
     constexpr int NT = WAVES_PREFILL * 64;
-    constexpr int KT = (FP8 || H < 16) ? 64 : 128;  // keys per LDS tile
-    constexpr int SPB = H >= 8 ? QPW : 8;  // score stores per 32-key block and wave
+    constexpr int KT = (!DMA || H < 16) ? 64 : 128;   // keys per LDS tile
+    constexpr int ROWB = Q8 ? G::ROWB8 : G::ROWB;     // LDS bytes per key row
+    constexpr int SCB = Q8 ? KT * 4 : 0;               // key scales after the rows (fp8 x fp8)
+    constexpr int SPB = H >= 8 ? QPW : 8;              // score stores per 32-key block and wave
 
-    __shared__ __attribute__((aligned(1024))) uint8_t sk0[KT * G::ROWB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sk1[KT * G::ROWB];
-    __shared__ float ssc[2][FP8 ? KT : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t sk0[KT * ROWB + SCB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sk1[KT * ROWB + SCB];
+    __shared__ float ssc[2][F == F_K8 ? KT : 1];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
     const int b = blockIdx.y;
@@ -224,7 +301,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     const int ntiles = (int)((n_keys + KT - 1) / KT);
     const uint8_t *kb = a.k + b * a.k_sb;
 
-    WaveRows<H, D> rows;
+    typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D>>::type rows;
     const int tq0 = t0 + wave * QPW;
     rows.load(a, b, tq0, lane);
 
@@ -234,23 +311,39 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     int pkey = -1;
     float pks = 1.f;
 
-    // One 32-key block of the tile at `tb`: B fragments from LDS, 16 MFMAs,
+    // One 32-key block of the tile at `tb`: B fragments from LDS, the MFMAs,
     // interleaved with the epilogue (ReLU * w, head reduction, store) of the
     // previous block.
     auto block = [&](const uint8_t *tb, int cb, float ksc, int key) {
-        const uint8_t *src = tb + (cb * 32 + l32) * G::ROWB + g * G::HALF * 2;
-        bf16x8 bk[G::KSTEPS];
-#pragma unroll
-        for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
+        const uint8_t *src = tb + (cb * 32 + l32) * ROWB + g * G::HALF * (Q8 ? 1 : 2);
         f32x16 acc0, acc1;
-        mfma_block<D>(rows.qa, bk, acc0, acc1);
+        if constexpr (Q8) {
+            i32x8 bk[G::KSTEPS8];
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS8; ++s) bk[s] = lds_ld32(src + 32 * s);
+            mfma_block8<D>(rows.qa, bk, acc0, acc1);
+        } else {
+            bf16x8 bk[G::KSTEPS];
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
+            mfma_block<D>(rows.qa, bk, acc0, acc1);
+        }
         const Part<H> pp = epi_reduce<H>(pa0, pa1, rows.wl, pks);
         // shape: the B-fragment reads, then MFMAs interleaved with VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, G::KSTEPS, 0);
+        if constexpr (Q8) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G::KSTEPS8 + 1, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * G::KSTEPS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int i = 0; i < 2 * G::KSTEPS8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            }
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, G::KSTEPS, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * G::KSTEPS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
         }
         // (columns past the last key are not stored: a tile may reach
         // beyond the row stride)
@@ -261,9 +354,9 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         pks = ksc;
     };
 
-    if constexpr (!FP8) {
-        constexpr int RS = G::ROWB / 16;     // 16-byte slots per LDS row (D/8 + 1 pad)
-        constexpr int NDMA = KT * RS / 64;   // 1 KB direct loads per tile
+    if constexpr (DMA) {
+        constexpr int RS = ROWB / 16;        // 16-byte slots per LDS row (row + 1 pad)
+        constexpr int NDMA = KT * RS / 64;   // 1 KB direct loads per tile (rows)
         constexpr int MPW = (NDMA + WAVES_PREFILL - 1) / WAVES_PREFILL;
         static_assert(KT * RS % 64 == 0, "tile must fill whole direct loads");
         // lane l of load m fills slot 64m + l = chunk c of tile row r (pad
@@ -277,18 +370,28 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         }
         auto gather = [&](int tile, uint8_t *dst) {
             const int64_t key0 = (int64_t)tile * KT;
+            const int64_t nk = min<int64_t>(n_keys - key0, KT);
             const uint8_t *tbase = kb + key0 * a.k_st;
-            const uint32_t bytes = (uint32_t)(min<int64_t>(n_keys - key0, KT) * a.k_st);
+            const uint32_t bytes = (uint32_t)(nk * a.k_st);
 #pragma unroll
             for (int i = 0; i < MPW; ++i) {
                 const int m = wave + WAVES_PREFILL * i;
                 if (m < NDMA) buffer_load_to_lds16(tbase, bytes, goff[i], dst + 1024 * m);
             }
+            if constexpr (Q8) {
+                // the tile's KT key scales (4 per lane), by the last wave
+                if (wave == WAVES_PREFILL - 1 && lane < KT / 4)
+                    buffer_load_to_lds16(a.k_scale + b * a.ks_sb + key0, (uint32_t)(nk * 4), 16 * lane,
+                                         dst + KT * ROWB);
+            }
         };
         auto step = [&](int it, const uint8_t *tb, uint8_t *nb) {
             if (it + 1 < ntiles) gather(it + 1, nb);
 #pragma unroll
-            for (int cb = 0; cb < KT / 32; ++cb) block(tb, cb, 1.f, it * KT + cb * 32 + l32);
+            for (int cb = 0; cb < KT / 32; ++cb) {
+                const float ksc = Q8 ? *reinterpret_cast<const float *>(tb + KT * ROWB + 4 * (cb * 32 + l32)) : 1.f;
+                block(tb, cb, ksc, it * KT + cb * 32 + l32);
+            }
             // this wave's loads into nb have landed (only the score stores
             // issued after them may still be in flight), then all waves' have
             wait_vmcnt<(KT / 32) * SPB>();
@@ -328,7 +431,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
                 const int c = tid + i * NT;
                 if (c >= SRC_CHUNKS) break;
                 const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
-                uint8_t *row = dst + kk * G::ROWB;
+                uint8_t *row = dst + kk * ROWB;
                 // 16 fp8 bytes -> 16 bf16 (32 bytes)
                 u32x2 lo0 = fp8x4_to_bf16x4(pf[i].x), lo1 = fp8x4_to_bf16x4(pf[i].y);
                 u32x2 hi0 = fp8x4_to_bf16x4(pf[i].z), hi1 = fp8x4_to_bf16x4(pf[i].w);
@@ -359,13 +462,15 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
 // 32-key blocks of that range, reading key fragments straight from HBM with
 // the next block's loads in flight while the current block computes.
 // ---------------------------------------------------------------------------
-template <int H, int D, bool FP8>
+template <int H, int D, int F>
 __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreArgs a)
 {
     using G = KeyGeom<D>;
+    constexpr bool Q8 = F == F_QK8;
+    constexpr bool K8 = F != F_BF16;
     constexpr int QPW = 64 / H;
     // per lane: G::HALF key elements = HALF*2 bytes (bf16) or HALF bytes (fp8)
-    constexpr int NLD = FP8 ? G::HALF / 16 : G::HALF / 8;  // 16-byte loads per lane per block
+    constexpr int NLD = K8 ? G::HALF / 16 : G::HALF / 8;  // 16-byte loads per lane per block
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
     const int b = blockIdx.z;
@@ -376,7 +481,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     if (key_lo >= key_hi) return;
     const int nblk = (int)((key_hi - key_lo + 31) / 32);
 
-    WaveRows<H, D> rows;
+    typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D>>::type rows;
     rows.load(a, b, tq0, lane);
     const uint8_t *kb = a.k + b * a.k_sb;
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
@@ -387,31 +492,41 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     auto fetch = [&](int blk, u32x4 (&r)[NLD], float &sc) {
         const int64_t key = key_lo + (int64_t)blk * 32 + l32;
         const bool ok = blk < nblk && key < key_hi;
-        const uint8_t *src = kb + key * a.k_st + g * (FP8 ? G::HALF : G::HALF * 2);
+        const uint8_t *src = kb + key * a.k_st + g * (K8 ? G::HALF : G::HALF * 2);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) r[i] = ok ? ld16(src + 16 * i) : u32x4{0, 0, 0, 0};
-        if constexpr (FP8) sc = ok ? a.k_scale[b * a.ks_sb + key] : 1.f;
+        if constexpr (K8) sc = ok ? a.k_scale[b * a.ks_sb + key] : 1.f;
     };
 
     int blk = wave;
     fetch(blk, cur, cs);
     for (; blk < nblk; blk += WAVES_SPLIT) {
         fetch(blk + WAVES_SPLIT, nxt, ns);
-        bf16x8 bk[G::KSTEPS];
-        if constexpr (FP8) {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                u32x2 p0 = fp8x4_to_bf16x4(cur[i].x), p1 = fp8x4_to_bf16x4(cur[i].y);
-                u32x2 p2 = fp8x4_to_bf16x4(cur[i].z), p3 = fp8x4_to_bf16x4(cur[i].w);
-                bk[2 * i] = as_bf16x8(u32x4{p0.x, p0.y, p1.x, p1.y});
-                bk[2 * i + 1] = as_bf16x8(u32x4{p2.x, p2.y, p3.x, p3.y});
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) bk[i] = as_bf16x8(cur[i]);
-        }
         f32x16 acc0, acc1;
-        mfma_block<D>(rows.qa, bk, acc0, acc1);
+        if constexpr (Q8) {
+            i32x8 bk[G::KSTEPS8];
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS8; ++s) {
+                const u32x4 lo = cur[2 * s], hi = cur[2 * s + 1];
+                bk[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            mfma_block8<D>(rows.qa, bk, acc0, acc1);
+        } else {
+            bf16x8 bk[G::KSTEPS];
+            if constexpr (K8) {
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    u32x2 p0 = fp8x4_to_bf16x4(cur[i].x), p1 = fp8x4_to_bf16x4(cur[i].y);
+                    u32x2 p2 = fp8x4_to_bf16x4(cur[i].z), p3 = fp8x4_to_bf16x4(cur[i].w);
+                    bk[2 * i] = as_bf16x8(u32x4{p0.x, p0.y, p1.x, p1.y});
+                    bk[2 * i + 1] = as_bf16x8(u32x4{p2.x, p2.y, p3.x, p3.y});
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) bk[i] = as_bf16x8(cur[i]);
+            }
+            mfma_block<D>(rows.qa, bk, acc0, acc1);
+        }
         const int64_t key = key_lo + (int64_t)blk * 32 + l32;
         epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), rs, key < key_hi, tq0, (int)key, lane);
 #pragma unroll
@@ -420,27 +535,35 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     }
 }
 
-template <int H, int D, bool FP8>
+template <int H, int D, int F>
 hipError_t launch_score_hd(const ScoreArgs &a, bool split, hipStream_t st)
 {
     constexpr int QPW = 64 / H;
     if (!split) {
         constexpr int QPB = WAVES_PREFILL * QPW;
         dim3 grid((a.T_q + QPB - 1) / QPB, a.B);
-        hipLaunchKernelGGL((score_prefill_kernel<H, D, FP8>), grid, dim3(WAVES_PREFILL * 64), 0, st, a);
+        hipLaunchKernelGGL((score_prefill_kernel<H, D, F>), grid, dim3(WAVES_PREFILL * 64), 0, st, a);
     } else {
         const int64_t n_keys = a.q_pos0 + a.T_q;
         dim3 grid((unsigned)((n_keys + a.key_split - 1) / a.key_split), (a.T_q + QPW - 1) / QPW, a.B);
-        hipLaunchKernelGGL((score_splitkey_kernel<H, D, FP8>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
+        hipLaunchKernelGGL((score_splitkey_kernel<H, D, F>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
     }
     return hipGetLastError();
+}
+
+template <int H, int D>
+hipError_t launch_score_f(const ScoreArgs &a, bool split, hipStream_t st)
+{
+    if (a.q8) return launch_score_hd<H, D, F_QK8>(a, split, st);
+    if (a.fp8) return launch_score_hd<H, D, F_K8>(a, split, st);
+    return launch_score_hd<H, D, F_BF16>(a, split, st);
 }
 
 template <int H>
 hipError_t launch_score_h(const ScoreArgs &a, bool split, hipStream_t st)
 {
-    if (a.D == 128) return a.fp8 ? launch_score_hd<H, 128, true>(a, split, st) : launch_score_hd<H, 128, false>(a, split, st);
-    return a.fp8 ? launch_score_hd<H, 64, true>(a, split, st) : launch_score_hd<H, 64, false>(a, split, st);
+    if (a.D == 128) return launch_score_f<H, 128>(a, split, st);
+    return launch_score_f<H, 64>(a, split, st);
 }
 
 }  // namespace

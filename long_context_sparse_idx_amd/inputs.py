@@ -46,6 +46,7 @@ class Workload:
     w_scale: float
     layer_noise: float     # per-layer q = q_0 + noise * eps_l (0: independent)
     seed: int = 0
+    q_fp8: bool = False    # indexer queries quantised to e4m3 per (token, head) (needs key_fp8)
 
     @property
     def n_layers(self):
@@ -105,6 +106,14 @@ WORKLOADS = {
 }
 
 
+# fp8 x fp8 variants: the same shapes with the indexer queries quantised to
+# e4m3 per (token, head) as well (the keys of the 200K variant become fp8 too).
+WORKLOADS["prefill1m_q8"] = dataclasses.replace(WORKLOADS["prefill1m"], name="prefill1m_q8", q_fp8=True)
+WORKLOADS["decode1m_q8"] = dataclasses.replace(WORKLOADS["decode1m"], name="decode1m_q8", q_fp8=True)
+WORKLOADS["prefill200k_q8"] = dataclasses.replace(WORKLOADS["prefill200k"], name="prefill200k_q8",
+                                                  key_fp8=True, q_fp8=True)
+
+
 def _seed(*parts) -> int:
     h = hashlib.sha256("/".join(str(p) for p in parts).encode()).digest()
     return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
@@ -133,7 +142,8 @@ def _draw(shape, kind, scale, device, *seed_parts, out_dtype=torch.bfloat16):
 
 
 def indexer_inputs(wl: Workload, layer: int, device, n_rows: Optional[int] = None):
-    """q_I [B, n_q, H_I, D_I] bf16, k_I [B, T_kv, D_I] (bf16, or fp8 bytes as
+    """q_I [B, n_q, H_I, D_I] bf16 (or, for q_fp8 workloads, fp8 bytes as uint8
+    with q_scale [B, n_q, H_I] fp32), k_I [B, T_kv, D_I] (bf16, or fp8 bytes as
     uint8 with k_scale [B, T_kv] fp32), w [B, n_q, H_I] fp32.
 
     Layer-dependent: with ``layer_noise`` > 0, q_I = q_0 + noise * eps_layer
@@ -144,14 +154,23 @@ def indexer_inputs(wl: Workload, layer: int, device, n_rows: Optional[int] = Non
     B, H, D = wl.B, wl.H_I, wl.D_I
     shared = wl.layer_noise > 0
     kl = 0 if shared else layer
-    q = _q_with_noise(wl, "q_I", (B * n_q, H, D), wl.q_I_scale, layer, device)
+    q = _q_with_noise(wl, "q_I", (B * n_q, H, D), wl.q_I_scale, layer, device,
+                      out_dtype=torch.float32 if wl.q_fp8 else torch.bfloat16)
+    q_scale = None
+    if wl.q_fp8:
+        # fp8 e4m3 queries: per-(token, head) scale = max|q| / 448 (a zero
+        # head gets 1), then q / scale cast to e4m3 (input preparation)
+        amax = q.abs().amax(dim=2)
+        q_scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (q / q_scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        q_scale = q_scale.view(B, n_q, H).contiguous()
     q = q.view(B, n_q, H, D)
     w = _draw((B * n_q, H), wl.w_dist, wl.w_scale, device, wl.seed, wl.name, "w", kl,
               out_dtype=torch.float32).view(B, n_q, H)
     if not wl.key_fp8:
         k = _draw((B * wl.T_kv, D), "normal", wl.k_I_scale, device, wl.seed, wl.name,
                   "k_I", kl).view(B, wl.T_kv, D)
-        return dict(q=q, k=k, k_scale=None, w=w)
+        return dict(q=q, k=k, k_scale=None, w=w, q_scale=q_scale)
     # fp8 e4m3 keys: per-token scale = max|k| / 448 (a zero row gets 1), then
     # k / scale cast to e4m3 (input preparation, not part of the method).
     kf = _draw((B * wl.T_kv, D), "normal", wl.k_I_scale, device, wl.seed, wl.name,
@@ -161,10 +180,10 @@ def indexer_inputs(wl: Workload, layer: int, device, n_rows: Optional[int] = Non
     k8 = (kf / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
     del kf
     return dict(q=q, k=k8.view(B, wl.T_kv, D), k_scale=scale.view(B, wl.T_kv).contiguous(),
-                w=w)
+                w=w, q_scale=q_scale)
 
 
-def _q_with_noise(wl, name, shape, scale, layer, device):
+def _q_with_noise(wl, name, shape, scale, layer, device, out_dtype=torch.bfloat16):
     if wl.layer_noise > 0:
         q = _draw(shape, "normal", scale, device, wl.seed, wl.name, name, 0,
                   out_dtype=torch.float32)
@@ -173,8 +192,8 @@ def _q_with_noise(wl, name, shape, scale, layer, device):
                         layer, out_dtype=torch.float32)
             q.add_(eps, alpha=wl.layer_noise)
             del eps
-        return q.to(torch.bfloat16)
-    return _draw(shape, "normal", scale, device, wl.seed, wl.name, name, layer)
+        return q.to(out_dtype)
+    return _draw(shape, "normal", scale, device, wl.seed, wl.name, name, layer, out_dtype=out_dtype)
 
 
 def attn_inputs(wl: Workload, layer: int, device, n_rows: Optional[int] = None):

@@ -26,6 +26,8 @@ LCSI_EALIGN = -5
 LCSI_EHIP = -6
 LCSI_KEY_BF16 = 0
 LCSI_KEY_FP8_E4M3 = 1
+LCSI_Q_BF16 = 0
+LCSI_Q_FP8_E4M3 = 1
 LCSI_SCORES_PRESET = 1
 LCSI_SCORES_ONLY = 2
 LCSI_MAX_TOPK = 2048
@@ -42,13 +44,14 @@ class LcsiError(RuntimeError):
 class Indexer(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T_q", ctypes.c_int32), ("T_kv", ctypes.c_int32),
                 ("H_I", ctypes.c_int32), ("D_I", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("key_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("key_dtype", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("q_pos0", ctypes.c_int64),
                 ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_st", ctypes.c_int64),
                 ("q_sh", ctypes.c_int64),
                 ("k", ctypes.c_void_p), ("k_sb", ctypes.c_int64), ("k_st", ctypes.c_int64),
                 ("k_scale", ctypes.c_void_p), ("ks_sb", ctypes.c_int64),
-                ("w", ctypes.c_void_p), ("w_sb", ctypes.c_int64), ("w_st", ctypes.c_int64)]
+                ("w", ctypes.c_void_p), ("w_sb", ctypes.c_int64), ("w_st", ctypes.c_int64),
+                ("q_scale", ctypes.c_void_p), ("qs_sb", ctypes.c_int64), ("qs_st", ctypes.c_int64)]
 
 
 class Attn(ctypes.Structure):
@@ -119,20 +122,26 @@ def _ws(nbytes: int, device) -> Optional[torch.Tensor]:
 # ------------------------------------------------------------- descriptors
 
 def indexer_desc(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, top_k: int, q_pos0: int,
-                 k_scale: Optional[torch.Tensor] = None, T_kv: Optional[int] = None) -> Indexer:
-    """q [B,T_q,H,D] bf16; k [B,T_kv,D] bf16 or fp8 e4m3 (uint8 / float8_e4m3fn
-    bytes) with k_scale [B,T_kv] fp32; w [B,T_q,H] fp32."""
+                 k_scale: Optional[torch.Tensor] = None, T_kv: Optional[int] = None,
+                 q_scale: Optional[torch.Tensor] = None) -> Indexer:
+    """q [B,T_q,H,D] bf16, or fp8 e4m3 bytes (uint8 / float8_e4m3fn) with
+    q_scale [B,T_q,H] fp32; k [B,T_kv,D] bf16 or fp8 e4m3 bytes with k_scale
+    [B,T_kv] fp32; w [B,T_q,H] fp32."""
     B, T_q, H, D = q.shape
     fp8 = k.dtype in (torch.uint8, torch.float8_e4m3fn)
+    q8 = q.dtype in (torch.uint8, torch.float8_e4m3fn)
     d = Indexer()
     d.B, d.T_q, d.H_I, d.D_I, d.top_k = B, T_q, H, D, top_k
     d.T_kv = k.shape[1] if T_kv is None else T_kv
     d.key_dtype = LCSI_KEY_FP8_E4M3 if fp8 else LCSI_KEY_BF16
+    d.q_dtype = LCSI_Q_FP8_E4M3 if q8 else LCSI_Q_BF16
     d.q_pos0 = q_pos0
     d.q, (d.q_sb, d.q_st, d.q_sh) = q.data_ptr(), q.stride()[:3]
     d.k, (d.k_sb, d.k_st) = k.data_ptr(), k.stride()[:2]
     if fp8:
         d.k_scale, d.ks_sb = k_scale.data_ptr(), k_scale.stride(0)
+    if q8:
+        d.q_scale, (d.qs_sb, d.qs_st) = q_scale.data_ptr(), q_scale.stride()[:2]
     d.w, (d.w_sb, d.w_st) = w.data_ptr(), w.stride()[:2]
     return d
 

@@ -64,8 +64,9 @@ class Workload:
             if not pattern[l]:
                 continue
             x = self.idx_in[l]
+            qs = x["q_scale"][:, r0:r0 + tq] if x["q_scale"] is not None else None
             ids.append(lcsi.indexer_desc(x["q"][:, r0:r0 + tq], x["k"], x["w"][:, r0:r0 + tq], wl.top_k, q0,
-                                         k_scale=x["k_scale"], T_kv=T_kv))
+                                         k_scale=x["k_scale"], T_kv=T_kv, q_scale=qs))
         ads = []
         for l in range(len(pattern)):
             x = self.attn_in[l]

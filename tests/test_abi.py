@@ -125,6 +125,20 @@ def test_indexer_fp8_needs_scale_and_16_byte_rows():
     assert call_idx(d)[0] == lcsi.LCSI_EALIGN                 # 136 B rows
 
 
+def test_indexer_fp8_queries_rules():
+    fp8k = dict(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE, ks_sb=100)
+    q8 = dict(q_dtype=lcsi.LCSI_Q_FP8_E4M3, q_scale=FAKE, qs_sb=16 * 64, qs_st=64)
+    assert call_idx(good_indexer(**fp8k, **q8))[0] == 0
+    assert call_idx(good_indexer(**fp8k, **{**q8, "q_dtype": 5}))[0] == lcsi.LCSI_EINVAL
+    assert call_idx(good_indexer(**q8))[0] == lcsi.LCSI_EUNSUPPORTED            # fp8 queries need fp8 keys
+    assert call_idx(good_indexer(**fp8k, **{**q8, "q_scale": 0}))[0] == lcsi.LCSI_EINVAL
+    assert call_idx(good_indexer(**fp8k, **{**q8, "q_scale": FAKE + 2}))[0] == lcsi.LCSI_EALIGN
+    assert call_idx(good_indexer(**fp8k, **{**q8, "qs_st": -1}))[0] == lcsi.LCSI_EINVAL
+    # fp8 query rows: strides in bytes, multiples of 16
+    assert call_idx(good_indexer(**fp8k, **q8, q_sh=136))[0] == lcsi.LCSI_EALIGN
+    assert call_idx(good_indexer(**fp8k, **q8, q_sh=144))[0] == 0
+
+
 def test_indexer_output_and_flags():
     need = call_idx(good_indexer())[1]
     # output checks apply when a workspace is given (not in query mode)

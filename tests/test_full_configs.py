@@ -49,7 +49,8 @@ def gpu_scores(run: Workload, layer, b, pos):
     for p in pos:
         r = p - wl.q_pos0
         d = lcsi.indexer_desc(x["q"][b:b + 1, r:r + 1], x["k"][b:b + 1], x["w"][b:b + 1, r:r + 1], wl.top_k, p,
-                              k_scale=x["k_scale"][b:b + 1] if x["k_scale"] is not None else None, T_kv=p + 1)
+                              k_scale=x["k_scale"][b:b + 1] if x["k_scale"] is not None else None, T_kv=p + 1,
+                              q_scale=x["q_scale"][b:b + 1, r:r + 1] if x["q_scale"] is not None else None)
         ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4, dtype=torch.float32, device="cuda")
         lcsi.idx_score_topk(d, None, ws, flags=lcsi.LCSI_SCORES_ONLY)
         torch.cuda.synchronize()
@@ -99,9 +100,13 @@ def check_workload(name, n_slots=None, batches=(0,), allf_overlap=False):
             g_idx = run.cache[fi % slots, b].index_select(0, rows_t).cpu().numpy()
             keys = x["k"][b].cpu().numpy() if wl.key_fp8 else u16(x["k"][b])
             ks = x["k_scale"][b].cpu().numpy() if wl.key_fp8 else None
-            q = u16(x["q"][b].index_select(0, rows_t))
+            if wl.q_fp8:
+                q = x["q"][b].index_select(0, rows_t).cpu().numpy()
+                qs = x["q_scale"][b].index_select(0, rows_t).cpu().numpy()
+            else:
+                q, qs = u16(x["q"][b].index_select(0, rows_t)), None
             w = x["w"][b].index_select(0, rows_t).cpu().numpy()
-            rS, r_idx = oracle.score_select(q, w, keys, np.array(pos, np.int64), wl.top_k, k_scale=ks)
+            rS, r_idx = oracle.score_select(q, w, keys, np.array(pos, np.int64), wl.top_k, k_scale=ks, q_scale=qs)
             gS = gpu_scores(run, layer, b, pos)
             for i, p in enumerate(pos):
                 check_scores(gS[i], rS[i, :p + 1], f"{name} b={b} F-layer {layer} p={p}")
@@ -150,3 +155,15 @@ def test_full_prefill1m():
 
 def test_full_decode1m():
     check_workload("decode1m", batches=(0, 7))
+
+
+def test_full_prefill1m_fp8_queries():
+    check_workload("prefill1m_q8")
+
+
+def test_full_decode1m_fp8_queries():
+    check_workload("decode1m_q8", batches=(0, 5))
+
+
+def test_full_prefill200k_fp8():
+    check_workload("prefill200k_q8")

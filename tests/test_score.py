@@ -5,8 +5,10 @@ score an exactly representable fp32 value whatever the summation order, so
 GPU scores must equal the oracle's bit for bit and the indices must match
 exactly.  Gaussian inputs are checked at the 1e-2 score tolerance and the
 near-tie rule for index sets.  Both score kernels (the LDS-staged prefill
-kernel and the split-key kernel used for few rows) and both key dtypes
-(bf16, fp8 e4m3 + scale) are covered, with ragged tails."""
+kernel and the split-key kernel used for few rows) and the three operand
+formats (bf16 keys; fp8 e4m3 keys + scale widened to bf16; fp8 keys and fp8
+queries + per-(token, head) scale on fp8 MFMA) are covered, with ragged
+tails."""
 import dataclasses
 
 import numpy as np
@@ -20,11 +22,11 @@ from helpers import bits, bytes_u8, check_index_sets, check_scores, log
 pytestmark = pytest.mark.gpu
 
 
-def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None):
+def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None, q_scale=None):
     """Returns (scores [B, T_q, ld] float32 host, idx [B, T_q, k] host)."""
     B, T_q = q.shape[:2]
     T_kv = k.shape[1]
-    d = lcsi.indexer_desc(q, k, w, top_k, q_pos0, k_scale=k_scale)
+    d = lcsi.indexer_desc(q, k, w, top_k, q_pos0, k_scale=k_scale, q_scale=q_scale)
     ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4, dtype=torch.float32, device="cuda")
     idx = torch.empty((B, T_q, top_k), dtype=torch.int32, device="cuda")
     lcsi.idx_score_topk(d, idx, ws)
@@ -34,10 +36,47 @@ def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None):
 
 def int_inputs(B, T_q, T_kv, H, D, seed):
     g = torch.Generator().manual_seed(seed)
-    q = torch.randint(-8, 9, (B, T_q, H, D), generator=g).to(torch.bfloat16)
+    q = torch.randint(-8, 9, (B, T_q, H, D), generator=g).to(torch.float32)
     k = torch.randint(-8, 9, (B, T_kv, D), generator=g).to(torch.float32)
     w = (2.0 ** torch.randint(-3, 1, (B, T_q, H), generator=g)).to(torch.float32)
     return q, k, w
+
+
+FORMATS = ["bf16", "k8", "qk8"]  # bf16 q/k; fp8 keys; fp8 keys and queries
+
+
+def encode(fmt, q, k, B, T_q, T_kv, H, g):
+    """Device operands and host copies in the format under test.  fp8 scales
+    are powers of two, so integer inputs stay exact."""
+    out = {}
+    if fmt == "bf16":
+        out["k"] = k.to(torch.bfloat16)
+        out["k_scale"] = None
+    else:
+        out["k"] = k.to(torch.float8_e4m3fn).view(torch.uint8)  # integers |x| <= 8 are exact in e4m3
+        out["k_scale"] = (2.0 ** torch.randint(-2, 2, (B, T_kv), generator=g)).to(torch.float32)
+    if fmt == "qk8":
+        out["q"] = q.to(torch.float8_e4m3fn).view(torch.uint8)
+        out["q_scale"] = (2.0 ** torch.randint(-2, 2, (B, T_q, H), generator=g)).to(torch.float32)
+    else:
+        out["q"] = q.to(torch.bfloat16)
+        out["q_scale"] = None
+    return out
+
+
+def host_q(x, b, rows):
+    """(q rows for the oracle, their scales or None)."""
+    if x["q"].dtype == torch.uint8:
+        return bytes_u8(x["q"][b, rows]), x["q_scale"][b, rows].numpy()
+    return bits(x["q"][b, rows]), None
+
+
+def host_k(x, b):
+    return bytes_u8(x["k"][b]) if x["k"].dtype == torch.uint8 else bits(x["k"][b])
+
+
+def dev(x, name):
+    return x[name].cuda() if x.get(name) is not None else None
 
 
 SHAPES = [
@@ -57,50 +96,48 @@ def check_rows(T_q):
     return sorted(x for x in r if 0 <= x < T_q)
 
 
-@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("shape", SHAPES)
-def test_score_integer_exact(shape, fp8):
+def test_score_integer_exact(shape, fmt):
     B, T_q, T_kv, q_pos0, H, D, k = shape
-    log(f"[score-int] shape={shape} fp8={fp8}")
-    q, kf, w = int_inputs(B, T_q, T_kv, H, D, seed=hash(shape) % 1000 + fp8)
-    if fp8:
-        kk = kf.to(torch.float8_e4m3fn)           # integers |x| <= 8 are exact in e4m3
-        scale = (2.0 ** torch.randint(-2, 2, (B, T_kv))).to(torch.float32)
-        kdev, sdev = kk.view(torch.uint8).cuda(), scale.cuda()
-    else:
-        kk = kf.to(torch.bfloat16)
-        kdev, sdev, scale = kk.cuda(), None, None
-    S, idx = gpu_indexer(q.cuda(), kdev, w.cuda(), k, q_pos0, k_scale=sdev)
+    log(f"[score-int] shape={shape} fmt={fmt}")
+    seed = hash(shape) % 1000 + FORMATS.index(fmt)
+    qf, kf, w = int_inputs(B, T_q, T_kv, H, D, seed=seed)
+    x = encode(fmt, qf, kf, B, T_q, T_kv, H, torch.Generator().manual_seed(seed + 7))
+    S, idx = gpu_indexer(dev(x, "q"), dev(x, "k"), w.cuda(), k, q_pos0, k_scale=dev(x, "k_scale"),
+                         q_scale=dev(x, "q_scale"))
     rows = check_rows(T_q)
     pos = np.array([q_pos0 + t for t in rows])
     for b in range(B):
-        keys = bytes_u8(kk[b]) if fp8 else bits(kk[b])
-        rS, ridx = oracle.score_select(bits(q[b, rows]), w[b, rows].numpy(), keys, pos, k,
-                                       k_scale=scale[b].numpy() if fp8 else None)
+        hq, hqs = host_q(x, b, rows)
+        rS, ridx = oracle.score_select(hq, w[b, rows].numpy(), host_k(x, b), pos, k,
+                                       k_scale=x["k_scale"][b].numpy() if x["k_scale"] is not None else None,
+                                       q_scale=hqs)
         for i, t in enumerate(rows):
             n = q_pos0 + t + 1
             assert np.array_equal(S[b, t, :n], rS[i, :n]), f"b={b} t={t}: scores differ"
             assert np.array_equal(idx[b, t], ridx[i]), f"b={b} t={t}: indices differ"
 
 
-@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("shape", SHAPES)
-def test_score_gaussian(shape, fp8):
+def test_score_gaussian(shape, fmt):
     B, T_q, T_kv, q_pos0, H, D, k = shape
-    log(f"[score-gauss] shape={shape} fp8={fp8}")
-    base = inputs.WORKLOADS["prefill1m" if fp8 else "prefill200k"]
+    log(f"[score-gauss] shape={shape} fmt={fmt}")
+    base = inputs.WORKLOADS[{"bf16": "prefill200k", "k8": "prefill1m", "qk8": "prefill1m_q8"}[fmt]]
     wl = dataclasses.replace(base, name=f"t{shape}", B=B, T_q=T_q, n_q=T_q, q_pos0=q_pos0,
                              T_kv=T_kv, H_I=H, D_I=D, top_k=k)
     x = inputs.indexer_inputs(wl, 0, "cpu")
-    S, idx = gpu_indexer(x["q"].cuda(), x["k"].cuda(), x["w"].cuda(), k, q_pos0,
-                         k_scale=x["k_scale"].cuda() if fp8 else None)
+    S, idx = gpu_indexer(dev(x, "q"), dev(x, "k"), dev(x, "w"), k, q_pos0, k_scale=dev(x, "k_scale"),
+                         q_scale=dev(x, "q_scale"))
     rows = check_rows(T_q)
     pos = np.array([q_pos0 + t for t in rows])
     swaps = 0
     for b in range(B):
-        keys = bytes_u8(x["k"][b]) if fp8 else bits(x["k"][b])
-        rS, ridx = oracle.score_select(bits(x["q"][b, rows]), x["w"][b, rows].numpy(), keys, pos, k,
-                                       k_scale=x["k_scale"][b].numpy() if fp8 else None)
+        hq, hqs = host_q(x, b, rows)
+        rS, ridx = oracle.score_select(hq, x["w"][b, rows].numpy(), host_k(x, b), pos, k,
+                                       k_scale=x["k_scale"][b].numpy() if x["k_scale"] is not None else None,
+                                       q_scale=hqs)
         for i, t in enumerate(rows):
             n = q_pos0 + t + 1
             check_scores(S[b, t, :n], rS[i, :n], f"b={b} t={t}")
@@ -123,19 +160,22 @@ def test_score_weight_scaling_and_h1_identity():
     assert np.array_equal(i1, i2)
 
 
-def test_prefill_and_splitkey_kernels_agree_bitwise():
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_prefill_and_splitkey_kernels_agree_bitwise(fmt):
     """The same rows scored as one batch of many rows (prefill kernel) and as
     single-row calls (split-key kernel) give identical bits: chunking never
     changes a score."""
     T_kv, H, D, k = 6000, 64, 128, 512
-    g = torch.Generator().manual_seed(9)
     T_q, q_pos0 = 2048, T_kv - 2048   # 256 workgroups: the prefill kernel
-    q = (torch.randn(1, T_q, H, D, generator=g) / 8).to(torch.bfloat16).cuda()
-    kk = (torch.randn(1, T_kv, D, generator=g) / 8).to(torch.bfloat16).cuda()
-    w = torch.rand(1, T_q, H, generator=g).cuda()
-    S_all, i_all = gpu_indexer(q, kk, w, k, q_pos0)
+    base = inputs.WORKLOADS[{"bf16": "prefill200k", "k8": "prefill1m", "qk8": "prefill1m_q8"}[fmt]]
+    wl = dataclasses.replace(base, name="agree", B=1, T_q=T_q, n_q=T_q, q_pos0=q_pos0, T_kv=T_kv,
+                             H_I=H, D_I=D, top_k=k)
+    x = {n: (v.cuda() if v is not None else None) for n, v in inputs.indexer_inputs(wl, 0, "cpu").items()}
+    S_all, i_all = gpu_indexer(x["q"], x["k"], x["w"], k, q_pos0, k_scale=x["k_scale"], q_scale=x["q_scale"])
     for t in (0, 17, 1000, 2047):
-        S1, i1 = gpu_indexer(q[:, t:t + 1], kk, w[:, t:t + 1], k, q_pos0 + t)
+        qs = x["q_scale"][:, t:t + 1] if x["q_scale"] is not None else None
+        S1, i1 = gpu_indexer(x["q"][:, t:t + 1], x["k"], x["w"][:, t:t + 1], k, q_pos0 + t,
+                             k_scale=x["k_scale"], q_scale=qs)
         n = q_pos0 + t + 1
         assert np.array_equal(S1[0, 0, :n], S_all[0, t, :n])
         assert np.array_equal(i1[0, 0], i_all[0, t])
