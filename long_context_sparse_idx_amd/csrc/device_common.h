@@ -41,24 +41,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// OCP E4M3 (fn variant) byte -> bf16 bits, exact for every finite code.
-// Normal codes (exponent field e >= 1): value (1 + m/8) 2^(e-7) keeps its
-// 3 mantissa bits and rebiases the exponent by 127 - 7 = 120.  Subnormal
-// codes (e == 0): value m * 2^-9, formed exactly through fp32.
-__device__ __forceinline__ uint32_t fp8e4m3_to_bf16_bits(uint32_t b)
-{
-    uint32_t em = b & 0x7Fu;
-    uint32_t r = em >= 8u ? (em << 4) + (120u << 7)
-                          : (__float_as_uint((float)em * 0x1p-9f) >> 16);
-    return r | ((b & 0x80u) << 8);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Four fp8 bytes (one dword) -> four bf16 values packed in two dwords.
+// Four OCP E4M3 bytes (one dword) -> four bf16 values packed in two dwords
+// (byte i -> half i), with the hardware conversion at scale 1.  Every finite
+// E4M3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is exactly a bf16
+// value, so the conversion is exact.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w)
 {
-    u32x2 r;
-    r.x = fp8e4m3_to_bf16_bits(w & 0xFFu) | (fp8e4m3_to_bf16_bits((w >> 8) & 0xFFu) << 16);
-    r.y = fp8e4m3_to_bf16_bits((w >> 16) & 0xFFu) | (fp8e4m3_to_bf16_bits(w >> 24) << 16);
+    u32x2 r{0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+#else
+    (void)w;
+#endif
     return r;
 }
 
