@@ -203,6 +203,25 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
                     float *ws, size_t *ws_bytes, void *const *events,
                     void *stream);
 
+/* Overlap of two layers' index sets, row by row: the statistic a search
+ * for which layers keep an indexer is driven by (adjacent layers select
+ * largely the same positions: IndexCache news article (app.myzaker.com),
+ * section "IndexCache"; the F/S split of an existing model is chosen
+ * greedily, layer by layer: IndexCache article after VentureBeat
+ * (linkstar.cloud), section on the two deployment routes).
+ *   a, b    device int32 index lists [B][T_q][top_k] (strides a_sb, a_st and
+ *           b_sb, b_st in elements), each row ascending with -1 padding at
+ *           the end, as idx_score_topk writes them.
+ *   counts  device int32 [B*T_q]: counts[b*T_q + t] = number of positions
+ *           (entries >= 0) present in both rows.
+ * Status as for the other calls (LCSI_EINVAL for null pointers, negative
+ * strides or sizes < 1; LCSI_EUNSUPPORTED for top_k > 2048; LCSI_EALIGN for
+ * pointers not 4-byte aligned).  Asynchronous on `stream`; no workspace. */
+int idx_overlap(const int32_t *a, int64_t a_sb, int64_t a_st,
+                const int32_t *b, int64_t b_sb, int64_t b_st,
+                int32_t B, int32_t T_q, int32_t top_k, int32_t *counts,
+                void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *lcsi_strerror(int code);
 

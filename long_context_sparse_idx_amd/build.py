@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblcsi.so")
-SOURCES = ["score.hip", "select.hip", "attn.hip", "api.hip"]
+SOURCES = ["score.hip", "select.hip", "attn.hip", "overlap.hip", "api.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

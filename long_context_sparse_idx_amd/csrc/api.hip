@@ -306,6 +306,28 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
     return LCSI_OK;
 }
 
+int idx_overlap(const int32_t *a, int64_t a_sb, int64_t a_st, const int32_t *b, int64_t b_sb, int64_t b_st,
+                int32_t B, int32_t T_q, int32_t top_k, int32_t *counts, void *stream)
+{
+    if (B < 1 || T_q < 1 || top_k < 1 || !counts) return LCSI_EINVAL;
+    if (top_k > LCSI_MAX_TOPK) return LCSI_EUNSUPPORTED;
+    int rc;
+    if ((rc = check_idx_out(a, a_sb, a_st)) || (rc = check_idx_out(b, b_sb, b_st))) return rc;
+    if (!aligned(counts, 4)) return LCSI_EALIGN;
+    OverlapArgs oa{};
+    oa.B = B;
+    oa.T_q = T_q;
+    oa.top_k = top_k;
+    oa.a = a;
+    oa.a_sb = a_sb;
+    oa.a_st = a_st;
+    oa.b = b;
+    oa.b_sb = b_sb;
+    oa.b_st = b_st;
+    oa.counts = counts;
+    return launch_overlap(oa, (hipStream_t)stream) == hipSuccess ? LCSI_OK : LCSI_EHIP;
+}
+
 const char *lcsi_strerror(int code)
 {
     switch (code) {

@@ -60,7 +60,17 @@ bool score_use_split(const ScoreArgs &a);
 int score_key_split(const ScoreArgs &a);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+struct OverlapArgs {
+    int B, T_q, top_k;
+    const int32_t *a;         // [B][T_q][top_k] ascending, -1 padded
+    int64_t a_sb, a_st;
+    const int32_t *b;
+    int64_t b_sb, b_st;
+    int32_t *counts;          // [B * T_q]
+};
+
 void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
+hipError_t launch_overlap(const OverlapArgs &a, hipStream_t st);
 
 }  // namespace lcsi

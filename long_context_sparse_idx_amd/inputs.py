@@ -47,6 +47,7 @@ class Workload:
     layer_noise: float     # per-layer q = q_0 + noise * eps_l (0: independent)
     seed: int = 0
     q_fp8: bool = False    # indexer queries quantised to e4m3 per (token, head) (needs key_fp8)
+    layer_walk: bool = False  # per-layer q = q_0 + noise * (eps_1 + ... + eps_l): a random walk
 
     @property
     def n_layers(self):
@@ -112,6 +113,14 @@ WORKLOADS["prefill1m_q8"] = dataclasses.replace(WORKLOADS["prefill1m"], name="pr
 WORKLOADS["decode1m_q8"] = dataclasses.replace(WORKLOADS["decode1m"], name="decode1m_q8", q_fp8=True)
 WORKLOADS["prefill200k_q8"] = dataclasses.replace(WORKLOADS["prefill200k"], name="prefill200k_q8",
                                                   key_fp8=True, q_fp8=True)
+
+
+# Layer-pattern search input: 12 indexer layers whose queries drift as a
+# random walk (q_l = q_{l-1} + 0.3 eps_l), so near layers select similar
+# positions and far ones less so; keys and weights shared by the layers.
+WORKLOADS["search32k"] = dataclasses.replace(
+    WORKLOADS["prefill32k"], name="search32k", pattern=tuple(1 if l % 4 == 0 else 0 for l in range(12)),
+    layer_walk=True)
 
 
 def _seed(*parts) -> int:
@@ -187,9 +196,9 @@ def _q_with_noise(wl, name, shape, scale, layer, device, out_dtype=torch.bfloat1
     if wl.layer_noise > 0:
         q = _draw(shape, "normal", scale, device, wl.seed, wl.name, name, 0,
                   out_dtype=torch.float32)
-        if layer > 0:
+        for j in (range(1, layer + 1) if wl.layer_walk else ([layer] if layer > 0 else [])):
             eps = _draw(shape, "normal", scale, device, wl.seed, wl.name, name + "_eps",
-                        layer, out_dtype=torch.float32)
+                        j, out_dtype=torch.float32)
             q.add_(eps, alpha=wl.layer_noise)
             del eps
         return q.to(out_dtype)

@@ -32,7 +32,7 @@ LCSI_SCORES_PRESET = 1
 LCSI_SCORES_ONLY = 2
 LCSI_MAX_TOPK = 2048
 
-EXPORTED = ("idx_score_topk", "sparse_attn", "run_layer_group", "lcsi_score_ld", "lcsi_strerror")
+EXPORTED = ("idx_score_topk", "sparse_attn", "run_layer_group", "idx_overlap", "lcsi_score_ld", "lcsi_strerror")
 
 
 class LcsiError(RuntimeError):
@@ -80,6 +80,8 @@ def _load():
     lib.run_layer_group.argtypes = [i32, p, ctypes.POINTER(Indexer), i32, ctypes.POINTER(Attn), p, i32,
                                     i64, i64, i64, p, sz, p, p]
     lib.run_layer_group.restype = i32
+    lib.idx_overlap.argtypes = [p, i64, i64, p, i64, i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, p, p]
+    lib.idx_overlap.restype = i32
     lib.lcsi_score_ld.argtypes = [ctypes.c_int32]
     lib.lcsi_score_ld.restype = i64
     lib.lcsi_strerror.argtypes = [i32]
@@ -249,3 +251,15 @@ def layer_group_ws_bytes(pattern, idx_descs, attn_descs, idx_cache, n_slots, slo
     _check(lib.run_layer_group(L, pat, ia, nf, aa, _ptr(idx_cache), n_slots, slot_stride, idx_sb, idx_st,
                                None, ctypes.byref(n), None, None), "run_layer_group(query)")
     return n.value
+
+
+def idx_overlap(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
+    """Per-row count of positions present in both index lists a, b
+    [B, T_q, k] int32 (ascending, -1 padded); returns int32 [B, T_q]."""
+    B, T_q, k = a.shape
+    assert b.shape == a.shape and a.dtype == b.dtype == torch.int32
+    assert a.stride(2) == 1 and b.stride(2) == 1, "index rows must be contiguous"
+    counts = torch.empty((B, T_q), dtype=torch.int32, device=a.device)
+    _check(lib.idx_overlap(_ptr(a), a.stride(0), a.stride(1), _ptr(b), b.stride(0), b.stride(1),
+                           B, T_q, k, _ptr(counts), _stream(stream)), "idx_overlap")
+    return counts

@@ -219,3 +219,15 @@ def layer_group(pattern, f_layers, attn_layers, pos, top_k, threads=None):
     if fi != len(f_layers):
         raise ValueError("number of F layers does not match the indexer inputs")
     return idx_per_layer, outs
+
+
+# ------------------------------------------------------------------ overlap
+
+def overlap_counts(a, b):
+    """Per row, the number of positions (entries >= 0) present in both index
+    lists: a, b int32 [R, k] -> int64 [R].  Plain set intersection."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape
+    return np.array([np.intersect1d(a[r][a[r] >= 0], b[r][b[r] >= 0]).size for r in range(a.shape[0])],
+                    np.int64)
