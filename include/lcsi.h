@@ -154,7 +154,10 @@ int64_t lcsi_score_ld(int32_t T_kv);
  * score_ws: fp32 workspace holding the head-reduced score rows,
  * [B][T_q][lcsi_score_ld(T_kv)], row (b,t) at (b*T_q + t)*ld; only entries
  * s <= p_t are defined.  Per-head scores are never written.  Its size is
- * B*T_q*ld*4 bytes (workspace rule above; it is always required).
+ * B*T_q*ld*4 bytes rounded up to 256, plus, when few long rows are selected
+ * (B*T_q <= 128 rows of >= 32768 keys: decode), the selection's candidate
+ * lists after the rows; query mode returns the total (workspace rule above;
+ * it is always required).
  * flags: LCSI_SCORES_PRESET selects from the scores the caller left in
  * score_ws (same layout) without scoring -- the hook for checking the
  * selection alone; LCSI_SCORES_ONLY stops after scoring (idx may be NULL).

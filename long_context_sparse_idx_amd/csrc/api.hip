@@ -79,9 +79,16 @@ int check_attn(const lcsi_attn *a)
     return LCSI_OK;
 }
 
+size_t score_rows_bytes(const lcsi_indexer *a)
+{
+    const size_t s = (size_t)a->B * (size_t)a->T_q * (size_t)score_ld(a->T_kv) * sizeof(float);
+    return (s + 255) / 256 * 256;
+}
+
+// score rows, then the selection's own part (few long rows only)
 size_t score_ws_bytes(const lcsi_indexer *a)
 {
-    return (size_t)a->B * (size_t)a->T_q * (size_t)score_ld(a->T_kv) * sizeof(float);
+    return score_rows_bytes(a) + select_ws_bytes(a->B, a->T_q, a->q_pos0);
 }
 
 size_t attn_ws_bytes(const lcsi_attn *a, int *splits_out = nullptr, int *split_len_out = nullptr)
@@ -178,7 +185,7 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
         se.idx = idx;
         se.idx_sb = idx_sb;
         se.idx_st = idx_st;
-        if (launch_select(se, s) != hipSuccess) return LCSI_EHIP;
+        if (launch_select(se, (uint8_t *)ws + score_rows_bytes(a), s) != hipSuccess) return LCSI_EHIP;
     }
     if (ev && record(ev, 1, s)) return LCSI_EHIP;
     return LCSI_OK;

@@ -34,6 +34,13 @@ struct SelectArgs {
     int64_t ld;
     int32_t *idx;
     int64_t idx_sb, idx_st;
+    // few long rows (set by launch_select from the workspace past the scores)
+    int nseg;                 // segments per row
+    int64_t seg_len;          // scores per segment
+    uint32_t *tau;            // [rows] sampled threshold key
+    int32_t *cnt;             // [rows][nseg] candidates per segment (-1: overflow)
+    uint32_t *ckey;           // [rows][nseg][cap] candidate keys
+    int32_t *cidx;            // [rows][nseg][cap] candidate positions
 };
 
 struct AttnArgs {
@@ -59,7 +66,11 @@ struct AttnArgs {
 bool score_use_split(const ScoreArgs &a);
 int score_key_split(const ScoreArgs &a);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
-hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+// Workspace bytes the selection needs past the score rows (0 unless few
+// long rows take the multi-workgroup path), and the launch (extra = that
+// part of the workspace).
+size_t select_ws_bytes(int B, int T_q, int64_t q_pos0);
+hipError_t launch_select(const SelectArgs &a, void *extra, hipStream_t st);
 struct OverlapArgs {
     int B, T_q, top_k;
     const int32_t *a;         // [B][T_q][top_k] ascending, -1 padded

@@ -22,6 +22,15 @@
 //     list overflows, the row falls back to C.  The result never depends on
 //     the sample, only the cost does.
 //  C  exact radix select and compaction streaming the row from memory.
+//
+// Few long rows (decode: a handful of sequences, each with up to a million
+// scores) would leave most of the chip idle with one workgroup per row, so
+// they take a three-kernel form of path B: one workgroup per row finds the
+// sampled threshold; many workgroups per row filter one segment each into
+// a per-segment candidate list in the workspace (ordered); one workgroup
+// per row gathers the lists (ascending positions, segment after segment)
+// and runs the exact select on them -- or path C when a segment overflowed
+// or fewer than k entries passed.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -287,10 +296,83 @@ struct GlobalSeg {
     }
 };
 
+// Threshold for the sampled pass over a row of n > NLDS scores: 8192 scores
+// in 32 evenly spaced runs of 256 give the key tau that about 2.5k entries
+// of the row are expected to reach.  Every thread returns tau.
+__device__ uint32_t sampled_threshold(Shared &sh, const float *row, int64_t n, int k)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int s = w * (NSB / NW); s < (w + 1) * (NSB / NW); ++s) {
+        const int64_t start = ((n - SBL) * s / (NSB - 1)) & ~(int64_t)3;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
+        uint32_t *d = sh.u.samp + s * SBL + 4 * lane;
+        d[0] = order_key(v.x);
+        d[1] = order_key(v.y);
+        d[2] = order_key(v.z);
+        d[3] = order_key(v.w);
+    }
+    __syncthreads();
+    int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
+    r = r < 1 ? 1 : (r > NSAMP ? NSAMP : r);
+    // a lower bound of the r-th sampled key, resolved to 1/256 of the
+    // samples' key range, is precise enough for a threshold -- unless its
+    // bin holds so many samples that the expected pass count would crowd
+    // the candidate lists (7/8 of their capacity); then refine further
+    const int64_t cap = (int64_t)NW * CAPW * 7 / 8 * NSAMP / n;
+    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r, 8, (int)(cap > r ? cap : r));
+    const uint32_t tau = sh.kth;
+    __syncthreads();  // every thread has read tau before the lists overwrite the samples
+    return tau;
+}
+
+// One streaming pass over row[lo, hi) (lo a multiple of 4): every entry with
+// key >= tau goes to its wave's ordered LDS list (wave w takes the w-th
+// contiguous part, a multiple of 256 entries long), so the lists visited
+// wave by wave are in ascending position order.  sh.wcnt[w] is the count of
+// wave w's passing entries (more than CAPW means its list overflowed).
+__device__ void filter_to_lists(Shared &sh, const float *row, int64_t lo_row, int64_t hi_row, uint32_t tau)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t seg = (hi_row - lo_row + NW * 256 - 1) / (NW * 256) * 256;
+    const int64_t lo = lo_row + (int64_t)w * seg;
+    const int64_t hi = min<int64_t>(hi_row, lo + seg);
+    int cnt = 0;
+    uint32_t *ck = sh.u.cand.key + w * CAPW;
+    int32_t *ci = sh.u.cand.idx + w * CAPW;
+    constexpr int U = 4;
+    for (int64_t base = lo; base < hi; base += U * 256) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * 256 + 4 * lane;
+            v[u] = i < hi ? *reinterpret_cast<const f32x4 *>(row + i) : f32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * 256 + 4 * lane;
+            const uint32_t k0 = order_key(v[u].x), k1 = order_key(v[u].y);
+            const uint32_t k2 = order_key(v[u].z), k3 = order_key(v[u].w);
+            const bool f0 = i < hi && k0 >= tau, f1 = i + 1 < hi && k1 >= tau;
+            const bool f2 = i + 2 < hi && k2 >= tau, f3 = i + 3 < hi && k3 >= tau;
+            const int c = (int)f0 + (int)f1 + (int)f2 + (int)f3;
+            if (ballot(c > 0) == 0) continue;
+            const uint64_t b0 = ballot(c & 1), b1 = ballot(c & 2), b2 = ballot(c & 4);
+            int p = cnt + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
+            if (f0) { if (p < CAPW) { ck[p] = k0; ci[p] = (int32_t)i; } ++p; }
+            if (f1) { if (p < CAPW) { ck[p] = k1; ci[p] = (int32_t)(i + 1); } ++p; }
+            if (f2) { if (p < CAPW) { ck[p] = k2; ci[p] = (int32_t)(i + 2); } ++p; }
+            if (f3) { if (p < CAPW) { ck[p] = k3; ci[p] = (int32_t)(i + 3); } ++p; }
+            cnt += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+        }
+    }
+    if (lane == 0) sh.wcnt[w] = cnt;
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 {
     __shared__ Shared sh;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int t = blockIdx.x, b = blockIdx.y;
     const int64_t n = a.q_pos0 + t + 1;
     const int k = a.top_k;
@@ -322,63 +404,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 
     // ---- path B: sampled threshold, one streaming pass, exact select on
     // the candidates
-    for (int s = w * (NSB / NW); s < (w + 1) * (NSB / NW); ++s) {
-        const int64_t start = ((n - SBL) * s / (NSB - 1)) & ~(int64_t)3;
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
-        uint32_t *d = sh.u.samp + s * SBL + 4 * lane;
-        d[0] = order_key(v.x);
-        d[1] = order_key(v.y);
-        d[2] = order_key(v.z);
-        d[3] = order_key(v.w);
-    }
-    __syncthreads();
-    int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
-    r = r < 1 ? 1 : (r > NSAMP ? NSAMP : r);
-    // a lower bound of the r-th sampled key, resolved to 1/256 of the
-    // samples' key range, is precise enough for a threshold -- unless its
-    // bin holds so many samples that the expected pass count would crowd
-    // the candidate lists (7/8 of their capacity); then refine further
-    const int64_t cap = (int64_t)NW * CAPW * 7 / 8 * NSAMP / n;
-    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r, 8, (int)(cap > r ? cap : r));
-    const uint32_t tau = sh.kth;
-    __syncthreads();  // every thread has read tau before the lists overwrite the samples
-
-    {
-        const int64_t seg = (n + NW * 256 - 1) / (NW * 256) * 256;
-        const int64_t lo = (int64_t)w * seg;
-        const int64_t hi = min<int64_t>(n, lo + seg);
-        int cnt = 0;
-        uint32_t *ck = sh.u.cand.key + w * CAPW;
-        int32_t *ci = sh.u.cand.idx + w * CAPW;
-        constexpr int U = 4;
-        for (int64_t base = lo; base < hi; base += U * 256) {
-            f32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t i = base + u * 256 + 4 * lane;
-                v[u] = i < hi ? *reinterpret_cast<const f32x4 *>(row + i) : f32x4{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t i = base + u * 256 + 4 * lane;
-                const uint32_t k0 = order_key(v[u].x), k1 = order_key(v[u].y);
-                const uint32_t k2 = order_key(v[u].z), k3 = order_key(v[u].w);
-                const bool f0 = i < hi && k0 >= tau, f1 = i + 1 < hi && k1 >= tau;
-                const bool f2 = i + 2 < hi && k2 >= tau, f3 = i + 3 < hi && k3 >= tau;
-                const int c = (int)f0 + (int)f1 + (int)f2 + (int)f3;
-                if (ballot(c > 0) == 0) continue;
-                const uint64_t b0 = ballot(c & 1), b1 = ballot(c & 2), b2 = ballot(c & 4);
-                int p = cnt + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
-                if (f0) { if (p < CAPW) { ck[p] = k0; ci[p] = (int32_t)i; } ++p; }
-                if (f1) { if (p < CAPW) { ck[p] = k1; ci[p] = (int32_t)(i + 1); } ++p; }
-                if (f2) { if (p < CAPW) { ck[p] = k2; ci[p] = (int32_t)(i + 2); } ++p; }
-                if (f3) { if (p < CAPW) { ck[p] = k3; ci[p] = (int32_t)(i + 3); } ++p; }
-                cnt += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-            }
-        }
-        if (lane == 0) sh.wcnt[w] = cnt;
-    }
-    __syncthreads();
+    const uint32_t tau = sampled_threshold(sh, row, n, k);
+    filter_to_lists(sh, row, 0, n, tau);
     int total = 0;
     bool overflow = false;
     for (int v = 0; v < NW; ++v) {
@@ -398,12 +425,167 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     emit(sh, GlobalSeg{row, n, seg}, out, k);
 }
 
+// ---------------------------------------------------------------------------
+// Few long rows: threshold / segment filter / final select.
+// ---------------------------------------------------------------------------
+constexpr int SEG_CAP = 2048;     // candidate slots per segment in the workspace
+
+__device__ __forceinline__ int64_t row_id(const SelectArgs &a, int b, int t) { return (int64_t)b * a.T_q + t; }
+
+__global__ __launch_bounds__(NT) void select_thresh_kernel(SelectArgs a)
+{
+    __shared__ Shared sh;
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int64_t n = a.q_pos0 + t + 1;
+    if (n <= a.top_k) return;
+    const float *row = a.S + row_id(a, b, t) * a.ld;
+    const uint32_t tau = sampled_threshold(sh, row, n, a.top_k);
+    if (threadIdx.x == 0) a.tau[row_id(a, b, t)] = tau;
+}
+
+__global__ __launch_bounds__(NT) void select_filter_kernel(SelectArgs a)
+{
+    __shared__ Shared sh;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int seg = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+    const int64_t n = a.q_pos0 + t + 1;
+    if (n <= a.top_k) return;
+    const int64_t r = row_id(a, b, t);
+    const int64_t lo = (int64_t)seg * a.seg_len;
+    const int64_t hi = min<int64_t>(n, lo + a.seg_len);
+    int32_t *cnt = a.cnt + r * a.nseg + seg;
+    if (lo >= hi) {
+        if (tid == 0) *cnt = 0;
+        return;
+    }
+    filter_to_lists(sh, a.S + r * a.ld, lo, hi, a.tau[r]);
+    int off = 0, total = 0;
+    bool overflow = false;
+    for (int v = 0; v < NW; ++v) {
+        if (v < w) off += sh.wcnt[v];
+        total += sh.wcnt[v];
+        overflow |= sh.wcnt[v] > CAPW;
+    }
+    if (overflow || total > SEG_CAP) {
+        if (tid == 0) *cnt = -1;
+        return;
+    }
+    uint32_t *ok = a.ckey + (r * a.nseg + seg) * SEG_CAP;
+    int32_t *oi = a.cidx + (r * a.nseg + seg) * SEG_CAP;
+    for (int j = lane; j < sh.wcnt[w]; j += 64) {
+        ok[off + j] = sh.u.cand.key[w * CAPW + j];
+        oi[off + j] = sh.u.cand.idx[w * CAPW + j];
+    }
+    if (tid == 0) *cnt = total;
+}
+
+__global__ __launch_bounds__(NT) void select_final_kernel(SelectArgs a)
+{
+    __shared__ Shared sh;
+    __shared__ int pre[65];
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int64_t n = a.q_pos0 + t + 1;
+    const int k = a.top_k;
+    const int64_t r = row_id(a, b, t);
+    const float *row = a.S + r * a.ld;
+    int32_t *out = a.idx + (int64_t)b * a.idx_sb + (int64_t)t * a.idx_st;
+    const int m = (int)min<int64_t>(n, k);
+    for (int j = m + tid; j < k; j += NT) out[j] = -1;
+    if (n <= k) {
+        for (int j = tid; j < m; j += NT) out[j] = j;
+        return;
+    }
+    if (tid == 0) {
+        int acc = 0;
+        bool bad = false;
+        for (int s = 0; s < a.nseg; ++s) {
+            const int c = a.cnt[r * a.nseg + s];
+            bad |= c < 0;
+            pre[s] = acc;
+            acc += c < 0 ? 0 : c;
+        }
+        pre[a.nseg] = bad ? -1 : acc;
+    }
+    __syncthreads();
+    const int total = pre[a.nseg];
+    if (total >= k && total <= NW * CAPW) {
+        // the concatenated lists, cut into NW consecutive parts: one per
+        // wave list, so the lists visited wave by wave stay ascending
+        const int per = (total + NW - 1) / NW;
+        for (int i = tid; i < total; i += NT) {
+            int s = 0;
+            while (pre[s + 1] <= i) ++s;  // segment holding entry i
+            const int64_t src = (r * a.nseg + s) * SEG_CAP + (i - pre[s]);
+            const int v = i / per, j = i - v * per;
+            sh.u.cand.key[v * CAPW + j] = a.ckey[src];
+            sh.u.cand.idx[v * CAPW + j] = a.cidx[src];
+        }
+        if (tid < NW) sh.wcnt[tid] = max(0, min(per, total - tid * per));
+        __syncthreads();
+        radix_find(sh, Candidates{&sh}, k);
+        emit(sh, CandSeg{&sh}, out, k);
+        return;
+    }
+    // path C: exact, streaming the row from memory
+    (void)w;
+    radix_find(sh, GlobalRow{row, n}, k);
+    const int64_t seg = ((n + NW - 1) / NW + 63) / 64 * 64;
+    emit(sh, GlobalSeg{row, n, seg}, out, k);
+}
+
+struct MultiPlan {
+    bool on;
+    int nseg;
+    int64_t seg_len;
+};
+
+MultiPlan multi_plan(int B, int T_q, int64_t q_pos0)
+{
+    const int64_t rows = (int64_t)B * T_q, n_max = q_pos0 + T_q;
+    if (rows > 128 || n_max < 32768) return {false, 1, 0};
+    int64_t nseg = (512 + rows - 1) / rows;
+    if (nseg > 64) nseg = 64;
+    int64_t seg = (n_max + nseg - 1) / nseg;
+    seg = (seg + NW * 256 - 1) / (NW * 256) * (NW * 256);
+    nseg = (n_max + seg - 1) / seg;
+    return {true, (int)nseg, seg};
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
-hipError_t launch_select(const SelectArgs &a, hipStream_t st)
+size_t select_ws_bytes(int B, int T_q, int64_t q_pos0)
 {
-    dim3 grid(a.T_q, a.B);
-    hipLaunchKernelGGL(select_kernel, grid, dim3(NT), 0, st, a);
+    const MultiPlan p = multi_plan(B, T_q, q_pos0);
+    if (!p.on) return 0;
+    const size_t rows = (size_t)B * T_q;
+    return align256(rows * 4) + align256(rows * p.nseg * 4) + 2 * align256(rows * p.nseg * SEG_CAP * 4);
+}
+
+hipError_t launch_select(const SelectArgs &a_in, void *extra, hipStream_t st)
+{
+    const MultiPlan p = multi_plan(a_in.B, a_in.T_q, a_in.q_pos0);
+    if (!p.on) {
+        hipLaunchKernelGGL(select_kernel, dim3(a_in.T_q, a_in.B), dim3(NT), 0, st, a_in);
+        return hipGetLastError();
+    }
+    SelectArgs a = a_in;
+    const size_t rows = (size_t)a.B * a.T_q;
+    uint8_t *ws = (uint8_t *)extra;
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    a.tau = (uint32_t *)ws;
+    ws += align256(rows * 4);
+    a.cnt = (int32_t *)ws;
+    ws += align256(rows * p.nseg * 4);
+    a.ckey = (uint32_t *)ws;
+    ws += align256(rows * p.nseg * SEG_CAP * 4);
+    a.cidx = (int32_t *)ws;
+    hipLaunchKernelGGL(select_thresh_kernel, dim3(a.T_q, a.B), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(select_filter_kernel, dim3(a.nseg, a.T_q, a.B), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(select_final_kernel, dim3(a.T_q, a.B), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 

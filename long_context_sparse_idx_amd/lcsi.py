@@ -173,9 +173,9 @@ def attn_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tens
 
 # -------------------------------------------------------------------- calls
 
-def idx_score_topk_ws_bytes(desc: Indexer) -> int:
+def idx_score_topk_ws_bytes(desc: Indexer, flags: int = 0) -> int:
     n = ctypes.c_size_t(0)
-    _check(lib.idx_score_topk(ctypes.byref(desc), None, 0, 0, None, ctypes.byref(n), 0, None),
+    _check(lib.idx_score_topk(ctypes.byref(desc), None, 0, 0, None, ctypes.byref(n), flags, None),
            "idx_score_topk(query)")
     return n.value
 

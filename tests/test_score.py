@@ -31,7 +31,8 @@ def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None, q_scale=None):
     idx = torch.empty((B, T_q, top_k), dtype=torch.int32, device="cuda")
     lcsi.idx_score_topk(d, idx, ws)
     torch.cuda.synchronize()
-    return ws.view(B, T_q, lcsi.score_ld(T_kv)).cpu().numpy(), idx.cpu().numpy()
+    ld = lcsi.score_ld(T_kv)
+    return ws[:B * T_q * ld].view(B, T_q, ld).cpu().numpy(), idx.cpu().numpy()
 
 
 def int_inputs(B, T_q, T_kv, H, D, seed):

@@ -17,11 +17,12 @@ pytestmark = pytest.mark.gpu
 def run_select(S_rows: np.ndarray, B: int, T_q: int, T_kv: int, q_pos0: int, k: int):
     """S_rows: float32 [B*T_q, n_max]; returns GPU idx [B*T_q, k]."""
     ld = lcsi.score_ld(T_kv)
-    ws = torch.zeros(B * T_q * ld, dtype=torch.float32, device="cuda")
-    wsv = ws.view(B * T_q, ld)
+    d = lcsi.preset_desc(B, T_q, T_kv, q_pos0, k)
+    # the score rows first; few long rows also use the space after them
+    ws = torch.zeros(max(B * T_q * ld, lcsi.idx_score_topk_ws_bytes(d, lcsi.LCSI_SCORES_PRESET) // 4), dtype=torch.float32, device="cuda")
+    wsv = ws[:B * T_q * ld].view(B * T_q, ld)
     wsv[:, :S_rows.shape[1]] = torch.from_numpy(S_rows).cuda()
     idx = torch.full((B, T_q, k), -7, dtype=torch.int32, device="cuda")
-    d = lcsi.preset_desc(B, T_q, T_kv, q_pos0, k)
     lcsi.idx_score_topk(d, idx, ws, flags=lcsi.LCSI_SCORES_PRESET)
     torch.cuda.synchronize()
     return idx.view(B * T_q, k).cpu().numpy()
@@ -65,6 +66,8 @@ def rows(rng, B, T_q, T_kv, kind):
     (1, 70, 70, 0, 64),           # n <= k, then LDS path (tiny workload's k)
     (1, 3, 100000, 99997, 1000),  # k not a power of two
     (3, 2, 20000, 19998, 1),      # k = 1
+    (4, 1, 300001, 300000, 2048), # few long rows: segment filters + final select
+    (1, 2, 70000, 69998, 2048),   # few long rows, 64 segments
 ])
 def test_select_bitexact(kind, shape):
     B, T_q, T_kv, q_pos0, k = shape
