@@ -295,14 +295,21 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
 
 }  // namespace
 
+#ifndef ATTN_SPLIT_TARGET
+#define ATTN_SPLIT_TARGET 256   // workgroups aimed at when few rows are present
+#endif
+#ifndef ATTN_MIN_TILES
+#define ATTN_MIN_TILES 2        // index tiles per split at least
+#endif
+
 void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len)
 {
     const int64_t rows = (int64_t)B * T_q;
     const int tiles = (top_k + TK - 1) / TK;
     int s = 1;
     if (rows < 256) {
-        s = (int)((256 + rows - 1) / rows);
-        const int max_s = (tiles + 1) / 2;  // keep >= 2 tiles per split
+        s = (int)((ATTN_SPLIT_TARGET + rows - 1) / rows);
+        const int max_s = (tiles + ATTN_MIN_TILES - 1) / ATTN_MIN_TILES;
         if (s > max_s) s = max_s;
         if (s < 1) s = 1;
     }

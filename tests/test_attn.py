@@ -67,6 +67,9 @@ CASES = [
     (3, 1, 5000, 4999, 64, 576, 512, True, 2048),   # decode: split + merge
     (2, 2, 3000, 2998, 32, 576, 512, True, 1000),
     (2, 1, 700, 699, 8, 128, 128, False, 333),
+    (1, 50, 1200, 1150, 20, 576, 512, False, 256),  # separate V of 512; 20 heads (partial group)
+    (1, 30, 400, 370, 1, 128, 128, False, 64),      # one head
+    (1, 33, 2000, 1967, 48, 576, 512, True, 700),   # 48 heads on the 64-head (8-wave) kernel
 ]
 
 
