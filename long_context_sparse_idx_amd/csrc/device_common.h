@@ -132,6 +132,38 @@ __device__ __forceinline__ void buffer_load_to_lds16(const void *base, uint32_t 
 #endif
 }
 
+// 16-byte load through a buffer resource over [base, base + bytes): bytes
+// past the end read as zero, so a guarded load needs no branch (and the
+// compiler can count outstanding loads exactly).  base and bytes
+// wave-uniform; bytes < 2^31.
+__device__ __forceinline__ u32x4 ld16_ranged(const void *base, uint32_t bytes, uint32_t off)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000),
+                                         (int)off, 0, 0));
+#else
+    (void)base;
+    (void)bytes;
+    (void)off;
+    return u32x4{0, 0, 0, 0};
+#endif
+}
+
+__device__ __forceinline__ float ld4_ranged(const void *base, uint32_t bytes, uint32_t off)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000),
+                                         (int)off, 0, 0));
+#else
+    (void)base;
+    (void)bytes;
+    (void)off;
+    return 0.f;
+#endif
+}
+
 // Workgroup barrier for LDS hand-offs only: no memory-model fence, so the
 // compiler does not wait for this wave's outstanding global stores or
 // direct-to-LDS loads (the caller waits for what it needs first); the empty

@@ -487,21 +487,32 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
     const RowSpan rs{Sb + (int64_t)tq0 * a.ld, (uint32_t)((min(a.T_q, tq0 + QPW) - tq0) * a.ld * 4), a.ld, tq0};
 
-    u32x4 cur[NLD], nxt[NLD];
-    float cs = 1.f, ns = 1.f;
-    auto fetch = [&](int blk, u32x4 (&r)[NLD], float &sc) {
-        const int64_t key = key_lo + (int64_t)blk * 32 + l32;
-        const bool ok = blk < nblk && key < key_hi;
-        const uint8_t *src = kb + key * a.k_st + g * (K8 ? G::HALF : G::HALF * 2);
+    // three register buffers: the blocks two and one steps ahead are in
+    // flight while the current one computes (the loop is unrolled by three so
+    // the buffers rotate by name, without copies)
+    u32x4 r0[NLD], r1[NLD], r2[NLD];
+    float s0 = 1.f, s1 = 1.f, s2 = 1.f;
+    // keys key_lo .. key_hi-1 through range-checked buffer loads: blocks and
+    // keys past the range read as zeros without a branch
+    const uint8_t *kr = kb + key_lo * a.k_st;
+    const uint32_t kr_bytes = (uint32_t)((key_hi - key_lo) * a.k_st);
+    const float *sr = K8 ? a.k_scale + b * a.ks_sb + key_lo : nullptr;
+    const uint32_t sr_bytes = (uint32_t)((key_hi - key_lo) * 4);
+    // Each buffer keeps its own running byte offsets (advanced by three
+    // blocks per use), so the load addresses live in registers of their own
+    // and never share one with a load still in flight.
+    const uint32_t kstride = (uint32_t)(3 * WAVES_SPLIT * 32) * (uint32_t)a.k_st;
+    const uint32_t sstride = 3 * WAVES_SPLIT * 32 * 4;
+    auto fetch = [&](uint32_t &koff, uint32_t &soff, u32x4 (&r)[NLD], float &sc) {
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) r[i] = ok ? ld16(src + 16 * i) : u32x4{0, 0, 0, 0};
-        if constexpr (K8) sc = ok ? a.k_scale[b * a.ks_sb + key] : 1.f;
+        for (int i = 0; i < NLD; ++i) r[i] = ld16_ranged(kr, kr_bytes, koff + 16 * i);
+        if constexpr (K8) sc = ld4_ranged(sr, sr_bytes, soff);
+        koff += kstride;
+        soff += sstride;
     };
-
-    int blk = wave;
-    fetch(blk, cur, cs);
-    for (; blk < nblk; blk += WAVES_SPLIT) {
-        fetch(blk + WAVES_SPLIT, nxt, ns);
+    auto step = [&](int blk, const u32x4 (&cur)[NLD], float cs, u32x4 (&ahead)[NLD], float &as, uint32_t &koff,
+                    uint32_t &soff) {
+        fetch(koff, soff, ahead, as);
         f32x16 acc0, acc1;
         if constexpr (Q8) {
             i32x8 bk[G::KSTEPS8];
@@ -529,9 +540,21 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
         }
         const int64_t key = key_lo + (int64_t)blk * 32 + l32;
         epi_store<H>(epi_reduce<H>(acc0, acc1, rows.wl, cs), rs, key < key_hi, tq0, (int)key, lane);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) cur[i] = nxt[i];
-        cs = ns;
+    };
+
+    int blk = wave;
+    const uint32_t kgo = g * (K8 ? G::HALF : G::HALF * 2);
+    uint32_t ko0 = (uint32_t)(blk * 32 + l32) * (uint32_t)a.k_st + kgo, so0 = (uint32_t)(blk * 32 + l32) * 4;
+    uint32_t ko1 = ko0 + (uint32_t)(WAVES_SPLIT * 32) * (uint32_t)a.k_st, so1 = so0 + WAVES_SPLIT * 32 * 4;
+    uint32_t ko2 = ko1 + (uint32_t)(WAVES_SPLIT * 32) * (uint32_t)a.k_st, so2 = so1 + WAVES_SPLIT * 32 * 4;
+    fetch(ko0, so0, r0, s0);
+    fetch(ko1, so1, r1, s1);
+    for (; blk < nblk; blk += 3 * WAVES_SPLIT) {
+        step(blk, r0, s0, r2, s2, ko2, so2);
+        if (blk + WAVES_SPLIT >= nblk) break;
+        step(blk + WAVES_SPLIT, r1, s1, r0, s0, ko0, so0);
+        if (blk + 2 * WAVES_SPLIT >= nblk) break;
+        step(blk + 2 * WAVES_SPLIT, r2, s2, r1, s1, ko1, so1);
     }
 }
 

@@ -125,6 +125,16 @@ def test_indexer_fp8_needs_scale_and_16_byte_rows():
     assert call_idx(d)[0] == lcsi.LCSI_EALIGN                 # 136 B rows
 
 
+def test_indexer_envelope_limits():
+    # the score rows of one workgroup (512 / H_I rows) must stay below 2 GiB
+    big = (1 << 31) // (4 * 512 // 4) + 64          # H_I = 4: 128 rows
+    assert call_idx(good_indexer(H_I=4, T_kv=big, q_pos0=big - 16, k_sb=big * 128))[0] == lcsi.LCSI_EUNSUPPORTED
+    assert call_idx(good_indexer(H_I=64, T_kv=big, q_pos0=big - 16, k_sb=big * 128))[0] == 0
+    # a 128-key tile of keys is addressed with 32-bit offsets: key rows below 16 MiB
+    assert call_idx(good_indexer(k_st=(1 << 23), k_sb=100 * (1 << 23)))[0] == lcsi.LCSI_EUNSUPPORTED
+    assert call_idx(good_indexer(k_st=(1 << 23) - 8, k_sb=100 * ((1 << 23) - 8)))[0] == 0
+
+
 def test_indexer_fp8_queries_rules():
     fp8k = dict(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE, ks_sb=100)
     q8 = dict(q_dtype=lcsi.LCSI_Q_FP8_E4M3, q_scale=FAKE, qs_sb=16 * 64, qs_st=64)

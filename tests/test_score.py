@@ -180,3 +180,28 @@ def test_prefill_and_splitkey_kernels_agree_bitwise(fmt):
         n = q_pos0 + t + 1
         assert np.array_equal(S1[0, 0, :n], S_all[0, t, :n])
         assert np.array_equal(i1[0, 0], i_all[0, t])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_degenerate_rows(fmt):
+    """One key (T_kv = 1) and very short causal rows mixing n <= k and n > k:
+    scores and indices as the oracle's, -1 padding after the n entries."""
+    for (T_q, T_kv, q_pos0, k) in [(1, 1, 0, 2048), (3, 3, 0, 2), (5, 7, 2, 1)]:
+        H, D = 64, 128
+        base = inputs.WORKLOADS[{"bf16": "prefill200k", "k8": "prefill1m", "qk8": "prefill1m_q8"}[fmt]]
+        wl = dataclasses.replace(base, name=f"deg{T_q}_{T_kv}", B=1, T_q=T_q, n_q=T_q, q_pos0=q_pos0,
+                                 T_kv=T_kv, H_I=H, D_I=D, top_k=k)
+        x = inputs.indexer_inputs(wl, 0, "cpu")
+        S, idx = gpu_indexer(dev(x, "q"), dev(x, "k"), dev(x, "w"), k, q_pos0, k_scale=dev(x, "k_scale"),
+                             q_scale=dev(x, "q_scale"))
+        rows = list(range(T_q))
+        hq, hqs = host_q(x, 0, rows)
+        pos = np.array([q_pos0 + t for t in rows])
+        rS, ridx = oracle.score_select(hq, x["w"][0, rows].numpy(), host_k(x, 0), pos, k,
+                                       k_scale=x["k_scale"][0].numpy() if x["k_scale"] is not None else None,
+                                       q_scale=hqs)
+        for t in rows:
+            n = q_pos0 + t + 1
+            check_scores(S[0, t, :n], rS[t, :n], f"T_kv={T_kv} t={t}")
+            assert np.array_equal(idx[0, t], ridx[t]), f"T_kv={T_kv} t={t}: {idx[0, t][:8]} vs {ridx[t][:8]}"
+            assert (idx[0, t, min(n, k):] == -1).all()
