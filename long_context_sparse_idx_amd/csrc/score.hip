@@ -370,7 +370,8 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         }
         auto gather = [&](int tile, uint8_t *dst) {
             const int64_t key0 = (int64_t)tile * KT;
-            const int64_t nk = min<int64_t>(n_keys - key0, KT);
+            const int64_t rem = n_keys - key0;
+            const int nk = rem < KT ? (int)rem : KT;  // keys of this tile
             const uint8_t *tbase = kb + key0 * a.k_st;
             const uint32_t bytes = (uint32_t)(nk * a.k_st);
 #pragma unroll
@@ -412,18 +413,23 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         constexpr int CPT = (SRC_CHUNKS + NT - 1) / NT;
         u32x4 pf[CPT];
         float pfs = 1.f;
+        // range-checked buffer loads: keys past the last one (and chunks past
+        // the tile) read as zeros without a branch, so the compiler can count
+        // the loads in flight exactly (a key's zero scale is never stored)
         auto fetch = [&](int tile) {
             const int64_t key0 = (int64_t)tile * KT;
+            const int64_t rem = n_keys - key0;
+            const int nk = rem <= 0 ? 0 : (rem < KT ? (int)rem : KT);  // keys of this tile (0 past the end)
+            const uint8_t *tbase = kb + key0 * a.k_st;
+            const uint32_t bytes = (uint32_t)(nk * a.k_st);
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 const int c = tid + i * NT;
                 const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
-                const int64_t key = key0 + kk;
-                pf[i] = u32x4{0, 0, 0, 0};
-                if (c < SRC_CHUNKS && key < n_keys) pf[i] = ld16(kb + key * a.k_st + part * 16);
+                const uint32_t off = c < SRC_CHUNKS ? (uint32_t)(kk * a.k_st + part * 16) : bytes;
+                pf[i] = ld16_ranged(tbase, bytes, off);
             }
-            const int64_t key = key0 + tid;
-            pfs = (tid < KT && key < n_keys) ? a.k_scale[b * a.ks_sb + key] : 1.f;
+            pfs = ld4_ranged(a.k_scale + b * a.ks_sb + key0, (uint32_t)(nk * 4), tid < KT ? 4 * tid : (uint32_t)(nk * 4));
         };
         auto stash = [&](uint8_t *dst, int buf) {
 #pragma unroll
@@ -443,13 +449,16 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         fetch(0);
         stash(sk0, 0);
         __syncthreads();
+        // (the tile after the last is fetched and stashed too -- as zeros,
+        // into the buffer nobody reads any more -- so the loop body has no
+        // branch around its loads and the compiler's wait counts stay exact)
         for (int it = 0; it < ntiles; ++it) {
             const int buf = it & 1;
-            if (it + 1 < ntiles) fetch(it + 1);
+            fetch(it + 1);
 #pragma unroll
             for (int cb = 0; cb < KT / 32; ++cb)
                 block(buf ? sk1 : sk0, cb, ssc[buf][cb * 32 + l32], it * KT + cb * 32 + l32);
-            if (it + 1 < ntiles) stash(buf ? sk0 : sk1, buf ^ 1);
+            stash(buf ? sk0 : sk1, buf ^ 1);
             __syncthreads();
         }
     }
