@@ -76,6 +76,7 @@ extern "C" {
 /* ------------------------------------------------------ idx_score_topk flags */
 #define LCSI_SCORES_PRESET 1u /* skip scoring: select from the scores already in score_ws */
 #define LCSI_SCORES_ONLY 2u   /* score only: leave the scores in score_ws, write no indices */
+#define LCSI_UNFUSED 4u       /* write every score row, then select (no fused candidate pass) */
 
 #define LCSI_MAX_TOPK 2048
 
@@ -156,12 +157,27 @@ int64_t lcsi_score_ld(int32_t T_kv);
  * s <= p_t are defined.  Per-head scores are never written.  Its size is
  * B*T_q*ld*4 bytes rounded up to 256, plus, when few long rows are selected
  * (B*T_q <= 128 rows of >= 32768 keys: decode), the selection's candidate
- * lists after the rows; query mode returns the total (workspace rule above;
- * it is always required).
+ * lists after the rows, plus, when the call takes the fused pass below,
+ * B*T_q*4 bytes (rounded up to 256) of counts and B*T_q*16384*8 bytes of
+ * candidate slots; query mode returns the total for the given flags
+ * (workspace rule above; it is always required).
+ *
+ * Fused pass (the default for H_I >= 16 when the prefill kernel runs, i.e.
+ * the rows fill the chip or have fewer than 4096 keys, and some row has
+ * more than top_k keys): score rows are not written.  The scoring kernel
+ * keeps, per row, only the scores at or above a threshold drawn from a
+ * sample of the row's scores (at most 16384 (score, position) pairs per
+ * row) and the selection runs on those; a row whose sample misjudged it
+ * (fewer than top_k or more than 16384 pairs) is rescored in full into
+ * score_ws and selected from there.  The indices are bit-identical to the
+ * unfused path (the same scores, the same selection rule); after a fused
+ * call score_ws holds no defined scores.
+ *
  * flags: LCSI_SCORES_PRESET selects from the scores the caller left in
  * score_ws (same layout) without scoring -- the hook for checking the
- * selection alone; LCSI_SCORES_ONLY stops after scoring (idx may be NULL).
- * Both set is LCSI_EINVAL.  With LCSI_SCORES_PRESET only B, T_q, T_kv,
+ * selection alone; LCSI_SCORES_ONLY stops after scoring (idx may be NULL);
+ * LCSI_UNFUSED writes every score row and selects from them.  PRESET and
+ * ONLY both set is LCSI_EINVAL.  With LCSI_SCORES_PRESET only B, T_q, T_kv,
  * q_pos0, top_k of `a` are read. */
 int idx_score_topk(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb,
                    int64_t idx_st, float *score_ws, size_t *ws_bytes,
@@ -179,7 +195,7 @@ int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
 
 /* The F/S layer loop over L layers (one conditional per layer):
  *   for l in 0..L-1:
- *     if pattern[l] (F): idx_score_topk(&idx_args[f], slot f % n_slots); f++
+ *     if pattern[l] (F): idx_score_topk(&idx_args[f], slot f % n_slots, flags 0); f++
  *     sparse_attn(&attn_args[l], current slot)
  * An S layer reads the slot written by the most recent F layer (the nearest
  * preceding F) and recomputes nothing.
@@ -195,7 +211,8 @@ int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
  *   ws / ws_bytes  one workspace for all steps (they run in order on one
  *              stream); query mode returns the largest single requirement.
  *   events     optional HOST array of 4*L hipEvent_t (as void*), or NULL.
- *              For layer l: [4l] before the layer, [4l+1] after scoring,
+ *              For layer l: [4l] before the layer, [4l+1] after scoring
+ *              (with the fused pass: after it and the rescoring launch),
  *              [4l+2] after selection, [4l+3] after attention (for an S
  *              layer the first three are recorded at the same point).
  * Pattern errors return LCSI_EPATTERN before anything is launched. */

@@ -85,10 +85,31 @@ size_t score_rows_bytes(const lcsi_indexer *a)
     return (s + 255) / 256 * 256;
 }
 
-// score rows, then the selection's own part (few long rows only)
-size_t score_ws_bytes(const lcsi_indexer *a)
+size_t align_ws(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+// Whether a call takes the fused candidate pass (see lcsi.h: LCSI_UNFUSED).
+bool fused_plan(const lcsi_indexer *a, unsigned flags)
 {
-    return score_rows_bytes(a) + select_ws_bytes(a->B, a->T_q, a->q_pos0);
+    if (flags & (LCSI_SCORES_PRESET | LCSI_SCORES_ONLY | LCSI_UNFUSED)) return false;
+    ScoreArgs sa{};
+    sa.B = a->B;
+    sa.T_q = a->T_q;
+    sa.H = a->H_I;
+    sa.q_pos0 = a->q_pos0;
+    sa.top_k = a->top_k;
+    return score_can_fuse(sa);
+}
+
+// score rows, then the selection's own part (few long rows only), then the
+// fused pass's counts and candidate slots
+size_t score_ws_bytes(const lcsi_indexer *a, unsigned flags)
+{
+    size_t s = score_rows_bytes(a) + select_ws_bytes(a->B, a->T_q, a->q_pos0);
+    if (fused_plan(a, flags)) {
+        const size_t rows = (size_t)a->B * (size_t)a->T_q;
+        s += align_ws(rows * 4) + rows * FUSE_CAP * 8;
+    }
+    return s;
 }
 
 size_t attn_ws_bytes(const lcsi_attn *a, int *splits_out = nullptr, int *split_len_out = nullptr)
@@ -140,6 +161,9 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
                 hipStream_t s, void *const *ev)
 {
     const int64_t ld = score_ld(a->T_kv);
+    const bool fused = fused_plan(a, flags);
+    const uint32_t *cand = nullptr;
+    const int32_t *ccnt = nullptr;
     if (!(flags & LCSI_SCORES_PRESET)) {
         ScoreArgs sa{};
         sa.B = a->B;
@@ -170,7 +194,23 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
         sa.S = ws;
         sa.ld = ld;
         sa.key_split = score_key_split(sa);
-        if (launch_score(sa, s) != hipSuccess) return LCSI_EHIP;
+        sa.top_k = a->top_k;
+        if (fused) {
+            uint8_t *fz = (uint8_t *)ws + score_rows_bytes(a) + select_ws_bytes(a->B, a->T_q, a->q_pos0);
+            sa.ccnt = (int32_t *)fz;
+            sa.cand = (uint32_t *)(fz + align_ws((size_t)a->B * a->T_q * 4));
+            sa.fuse = 1;
+            if (launch_score(sa, s) != hipSuccess) return LCSI_EHIP;
+            // full rows for the workgroups holding a row the candidates
+            // cannot settle (usually none: then every workgroup exits at once)
+            sa.fuse = 0;
+            sa.redo = sa.ccnt;
+            if (launch_score(sa, s) != hipSuccess) return LCSI_EHIP;
+            cand = sa.cand;
+            ccnt = sa.ccnt;
+        } else if (launch_score(sa, s) != hipSuccess) {
+            return LCSI_EHIP;
+        }
     }
     if (ev && record(ev, 0, s)) return LCSI_EHIP;
     if (!(flags & LCSI_SCORES_ONLY)) {
@@ -185,6 +225,8 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
         se.idx = idx;
         se.idx_sb = idx_sb;
         se.idx_st = idx_st;
+        se.cand = cand;
+        se.ccnt = ccnt;
         if (launch_select(se, (uint8_t *)ws + score_rows_bytes(a), s) != hipSuccess) return LCSI_EHIP;
     }
     if (ev && record(ev, 1, s)) return LCSI_EHIP;
@@ -239,13 +281,14 @@ int64_t lcsi_score_ld(int32_t T_kv) { return score_ld(T_kv < 0 ? 0 : T_kv); }
 int idx_score_topk(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx_st, float *score_ws,
                    size_t *ws_bytes, unsigned flags, void *stream)
 {
-    if (flags & ~(LCSI_SCORES_PRESET | LCSI_SCORES_ONLY)) return LCSI_EINVAL;
+    if (flags & ~(LCSI_SCORES_PRESET | LCSI_SCORES_ONLY | LCSI_UNFUSED)) return LCSI_EINVAL;
     if ((flags & LCSI_SCORES_PRESET) && (flags & LCSI_SCORES_ONLY)) return LCSI_EINVAL;
     int rc = check_indexer(a, flags & LCSI_SCORES_PRESET);
     if (rc) return rc;
-    if (!score_ws && ws_bytes) return workspace_rule(score_ws, ws_bytes, score_ws_bytes(a)) < 0 ? LCSI_EINVAL : LCSI_OK;
+    if (!score_ws && ws_bytes)
+        return workspace_rule(score_ws, ws_bytes, score_ws_bytes(a, flags)) < 0 ? LCSI_EINVAL : LCSI_OK;
     if (!(flags & LCSI_SCORES_ONLY) && (rc = check_idx_out(idx, idx_sb, idx_st))) return rc;
-    rc = workspace_rule(score_ws, ws_bytes, score_ws_bytes(a));
+    rc = workspace_rule(score_ws, ws_bytes, score_ws_bytes(a, flags));
     if (rc) return rc < 0 ? rc : LCSI_OK;
     return run_indexer(a, idx, idx_sb, idx_st, score_ws, flags, (hipStream_t)stream, nullptr);
 }
@@ -279,7 +322,7 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
         const lcsi_indexer *x = &idx_args[f];
         if ((rc = check_indexer(x, false))) return rc;
         if (x->B != a0->B || x->T_q != a0->T_q || x->q_pos0 != a0->q_pos0 || x->top_k != a0->top_k) return LCSI_EINVAL;
-        const size_t s = score_ws_bytes(x);
+        const size_t s = score_ws_bytes(x, 0u);
         need = s > need ? s : need;
     }
     for (int l = 0; l < L; ++l) {

@@ -97,6 +97,20 @@ __device__ __forceinline__ void store_b32_ranged(float *base, uint32_t bytes, ui
 #endif
 }
 
+// 64-bit store through a buffer resource, with the same range rule as above.
+__device__ __forceinline__ void store_b64_ranged(void *base, uint32_t bytes, uint32_t off, u32x2 v)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b64(v, __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000), (int)off,
+                                          0, 0);
+#else
+    (void)base;
+    (void)bytes;
+    (void)off;
+    (void)v;
+#endif
+}
+
 // Direct global->LDS load (global_load_lds_dwordx4): every lane loads 16
 // bytes from its own address; lane l's bytes land at lds + 16*l (lds is
 // wave-uniform).  The builtin is only spelled out for the device pass: in

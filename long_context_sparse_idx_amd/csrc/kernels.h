@@ -25,7 +25,30 @@ struct ScoreArgs {
     float *S;                 // [B][T_q][ld]
     int64_t ld;
     int key_split;            // keys per workgroup (split-key kernel)
+    int top_k;
+    // fused selection (prefill kernel, H >= 16): instead of S, each row's
+    // scores at or above a sampled threshold go to cand as ascending
+    // (score bits, position) pairs, at most FUSE_CAP per row, and ccnt gets
+    // the row's count (FUSE_CAP + 1 and above: overflow)
+    int fuse;
+    uint32_t *cand;           // [B * T_q][FUSE_CAP][2]
+    int32_t *ccnt;            // [B * T_q]
+    // rescoring after a fused pass (unfused prefill kernel): when set, a
+    // workgroup runs only if one of its rows has a count the selection
+    // cannot use (fused_row_bad), and then writes its full rows to S
+    const int32_t *redo;      // [B * T_q] counts of the fused pass, or null
 };
+
+// Candidate slots per row of the fused selection.
+constexpr int FUSE_CAP = 16384;
+
+// A fused row of n scores whose count c the selection cannot use: fewer
+// candidates than the top-k (the sampled threshold was too high) or more
+// than the slots hold.  Rows with n <= k need no selection at all.
+__host__ __device__ inline bool fused_row_bad(int32_t c, int64_t n, int k)
+{
+    return n > k && (c < k || c > FUSE_CAP);
+}
 
 struct SelectArgs {
     int B, T_q, top_k;
@@ -41,6 +64,10 @@ struct SelectArgs {
     int32_t *cnt;             // [rows][nseg] candidates per segment (-1: overflow)
     uint32_t *ckey;           // [rows][nseg][cap] candidate keys
     int32_t *cidx;            // [rows][nseg][cap] candidate positions
+    // after a fused score pass: the candidate pairs and counts (ScoreArgs);
+    // rows with a usable count select from them, the others from S
+    const uint32_t *cand;
+    const int32_t *ccnt;
 };
 
 struct AttnArgs {
@@ -64,6 +91,8 @@ struct AttnArgs {
 };
 
 bool score_use_split(const ScoreArgs &a);
+// Whether a call with these arguments can take the fused selection.
+bool score_can_fuse(const ScoreArgs &a);
 int score_key_split(const ScoreArgs &a);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
 // Workspace bytes the selection needs past the score rows (0 unless few

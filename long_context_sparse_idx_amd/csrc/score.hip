@@ -144,56 +144,77 @@ struct Part {
     float v[N];
 };
 
+// The epilogue in 32 units, one per accumulator value r of this lane
+// (acc0[r] for r < 16, else acc1[r - 16]): unit r adds w * max(0, x) to its
+// partial sum.  Units run in ascending r (the prefill kernel spreads them
+// over the MFMAs of the next block), then finish() adds the partials.
+template <int H>
+struct EpiAcc {
+    static constexpr int QPW = H >= 8 ? 64 / H : 1;
+    static constexpr int E = 32 / QPW;                                       // units per query (H >= 8)
+    static constexpr int NP = H >= 8 ? (E >= 16 ? 8 : (E >= 8 ? 4 : 2)) : 1;  // partial sums per query
+    static constexpr int NQ = H >= 8 ? QPW : 8;                              // queries of this lane
+    float ps[NQ][NP];
+
+    __device__ __forceinline__ void init()
+    {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int j = 0; j < NP; ++j) ps[q][j] = 0.f;
+    }
+
+    __device__ __forceinline__ void unit(int r, const f32x16 &acc0, const f32x16 &acc1, const float (&wl)[2][16])
+    {
+        const float m = fmaxf(r < 16 ? acc0[r] : acc1[r - 16], 0.f);
+        const float wv = wl[r >> 4][r & 15];
+        if constexpr (H >= 8) {
+            // Each query owns E accumulator values of this lane, summed into
+            // NP independent partial sums (element e goes to partial e % NP),
+            // so the VALU never waits on one long dependent chain.
+            const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2);  // first row of r's group of 4
+            const int q = row / H;
+            const int e = r - q * E;                               // element index within query q
+            ps[q][e % NP] = __builtin_fmaf(wv, m, ps[q][e % NP]);
+        } else {
+            static_assert(H == 4, "H must be 4, 8, 16, 32 or 64");
+            // rows 8j + 4g + i of tile rt are the 4 heads of query 8*rt + 2j + g
+            const int rt = r >> 4, j = (r & 15) >> 2;
+            ps[rt * 4 + j][0] = __builtin_fmaf(wv, m, ps[rt * 4 + j][0]);
+        }
+    }
+
+    // the partials added as a balanced tree, the lane halves summed (H >= 8),
+    // the key scale applied
+    __device__ __forceinline__ Part<H> finish(float kscale)
+    {
+        Part<H> p;
+        if constexpr (H >= 8) {
+#pragma unroll
+            for (int q = 0; q < QPW; ++q) {
+#pragma unroll
+                for (int w = NP / 2; w >= 1; w >>= 1)
+#pragma unroll
+                    for (int j = 0; j < w; ++j) ps[q][j] += ps[q][j + w];
+                p.v[q] = sum_lane_halves(ps[q][0]) * kscale;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p.v[i] = ps[i][0] * kscale;
+        }
+        return p;
+    }
+};
+
 template <int H>
 __device__ __forceinline__ Part<H> epi_reduce(const f32x16 &acc0, const f32x16 &acc1, const float (&wl)[2][16],
                                               float kscale)
 {
-    Part<H> p;
-    if constexpr (H >= 8) {
-        // Each query owns E = 32/QPW accumulator values of this lane; they are
-        // summed into NP independent partial sums (element e goes to partial
-        // e % NP) and the partials are added as a balanced tree, so the VALU
-        // never waits on one long dependent chain.
-        constexpr int QPW = 64 / H;
-        constexpr int E = 32 / QPW;
-        constexpr int NP = E >= 16 ? 8 : (E >= 8 ? 4 : 2);
-        float ps[QPW][NP];
+    EpiAcc<H> e;
+    e.init();
 #pragma unroll
-        for (int q = 0; q < QPW; ++q)
-#pragma unroll
-            for (int j = 0; j < NP; ++j) ps[q][j] = 0.f;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2);  // first row of r's group of 4
-            const int q = row / H;
-            const int e = r - q * E;                               // element index within query q
-            const float x = r < 16 ? acc0[r] : acc1[r - 16];
-            ps[q][e % NP] += wl[r >> 4][r & 15] * fmaxf(x, 0.f);
-        }
-#pragma unroll
-        for (int q = 0; q < QPW; ++q) {
-#pragma unroll
-            for (int w = NP / 2; w >= 1; w >>= 1)
-#pragma unroll
-                for (int j = 0; j < w; ++j) ps[q][j] += ps[q][j + w];
-            p.v[q] = sum_lane_halves(ps[q][0]) * kscale;
-        }
-    } else {
-        static_assert(H == 4, "H must be 4, 8, 16, 32 or 64");
-        // rows 8j + 4g + i (i < 4) of tile rt are the 4 heads of query 8*rt + 2j + g
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x16 &acc = rt == 0 ? acc0 : acc1;
-                float v = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v += wl[rt][4 * j + i] * fmaxf(acc[4 * j + i], 0.f);
-                p.v[rt * 4 + j] = v * kscale;
-            }
-        }
-    }
-    return p;
+    for (int r = 0; r < 32; ++r) e.unit(r, acc0, acc1, wl);
+    return e.finish(kscale);
 }
 
 // Rows of the score matrix a workgroup writes: rows t_lo .. t_lo + n - 1
@@ -274,8 +295,50 @@ __device__ __forceinline__ void mfma_block8(const i32x8 (&qa)[2][KeyGeom<D>::KST
 // Inside each wave the MFMAs of a 32-key block overlap the epilogue of the
 // previous block (software pipeline; the accumulators of block j-1 wait in
 // pa0/pa1 while block j runs).
+//
+// Fused selection (FUSE, H >= 16): instead of the score row, the kernel
+// writes each row's candidates for the top-k.
+//   1. Sample: when the workgroup's longest row has more than FUSE_CAP keys,
+//      it first scores NS whole tiles spread evenly over the keys that all
+//      its rows cover (SPQ keys per query row) into LDS, and each wave takes,
+//      for each of its query rows, the r-th largest sampled score as the
+//      row's threshold tau.  r is the expected number of sampled scores at
+//      or above the row's k-th largest, plus 4.5 standard deviations and 2,
+//      so that the top-k lies at or above tau with high probability while
+//      the number of scores at or above tau stays far below FUSE_CAP.  Rows
+//      of shorter workgroups keep every score (tau = -inf).
+//   2. Sweep: the full causal sweep, whose epilogue writes every score >= tau
+//      of a key at or before the row's position as a (score bits, position)
+//      pair to the row's candidate slots, in ascending position order (one
+//      ballot and prefix count per 32-key block), and at the end the count.
+// Every score that reaches the row's k-th largest is a candidate whenever
+// the count is at least k, so the top-k of the candidates is the top-k of
+// the row.  A count below k or above FUSE_CAP only costs time: the caller
+// rescores those rows in full (fused_row_bad).
 // ---------------------------------------------------------------------------
-template <int H, int D, int F>
+constexpr int FUSE_SAMPLES = 16384;  // sampled scores per workgroup (64 KB of LDS)
+
+template <int SPQ>
+__device__ __forceinline__ float sample_threshold(const float *s, int r, int lane)
+{
+    // the r-th largest of the SPQ sampled keys, bit by bit from the top: the
+    // largest key T that at least r samples reach
+    uint32_t kk[SPQ / 64];
+#pragma unroll
+    for (int j = 0; j < SPQ / 64; ++j) kk[j] = order_key(s[64 * j + lane]);
+    uint32_t T = 0;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < SPQ / 64; ++j) cnt += __popcll(ballot(kk[j] >= c));
+        if (cnt >= r) T = c;
+    }
+    return __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
+}
+
+template <int H, int D, int F, bool FUSE>
 __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(ScoreArgs a)
 {
     using G = KeyGeom<D>;
@@ -288,18 +351,36 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     constexpr int ROWB = Q8 ? G::ROWB8 : G::ROWB;     // LDS bytes per key row
     constexpr int SCB = Q8 ? KT * 4 : 0;               // key scales after the rows (fp8 x fp8)
     constexpr int SPB = H >= 8 ? QPW : 8;              // score stores per 32-key block and wave
+    constexpr int SPQ = FUSE ? FUSE_SAMPLES / QPB : 64;  // sampled keys per query row
+    constexpr int NS = SPQ / KT;                       // sampled tiles
+    static_assert(!FUSE || (H >= 16 && SPQ % KT == 0 && SPQ % 64 == 0), "fused sample shape");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sk0[KT * ROWB + SCB];
     __shared__ __attribute__((aligned(1024))) uint8_t sk1[KT * ROWB + SCB];
     __shared__ float ssc[2][F == F_K8 ? KT : 1];
+    __shared__ float samp[FUSE ? FUSE_SAMPLES : 1];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    // (the wave index as a scalar: addresses built from it, such as a
+    // buffer resource, are then known to be the same in every lane)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+              g = lane >> 5;
     const int b = blockIdx.y;
     const int t0 = (gridDim.x - 1 - blockIdx.x) * QPB;
     const int t_end = min(a.T_q, t0 + QPB);
     const int64_t n_keys = a.q_pos0 + t_end;
     const int ntiles = (int)((n_keys + KT - 1) / KT);
     const uint8_t *kb = a.k + b * a.k_sb;
+
+    if constexpr (!FUSE) {
+        // rescoring after a fused pass: only workgroups holding a row whose
+        // candidates the selection cannot use
+        if (a.redo) {
+            bool any = false;
+            for (int t = t0; t < t_end; ++t)
+                any |= fused_row_bad(a.redo[(int64_t)b * a.T_q + t], a.q_pos0 + t + 1, a.top_k);
+            if (!any) return;
+        }
+    }
 
     typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D>>::type rows;
     const int tq0 = t0 + wave * QPW;
@@ -312,157 +393,242 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     float pks = 1.f;
 
     // One 32-key block of the tile at `tb`: B fragments from LDS, the MFMAs,
-    // interleaved with the epilogue (ReLU * w, head reduction, store) of the
-    // previous block.
-    auto block = [&](const uint8_t *tb, int cb, float ksc, int key) {
+    // interleaved with the epilogue (ReLU * w, head reduction) of the
+    // previous block, whose reduced scores go to `sink` with that block's
+    // key (-1 before the first block).  The interleave is fixed in the code:
+    // each MFMA is followed by its share of the epilogue units and a
+    // scheduling barrier, so the VALU work of one wave fills the MFMA
+    // pipeline's shadow whatever the surrounding control flow.
+    auto block = [&](const uint8_t *tb, int cb, float ksc, int key, auto &sink) {
         const uint8_t *src = tb + (cb * 32 + l32) * ROWB + g * G::HALF * (Q8 ? 1 : 2);
-        f32x16 acc0, acc1;
+        f32x16 acc0 = f32x16{0}, acc1 = f32x16{0};
+        EpiAcc<H> ea;
+        ea.init();
         if constexpr (Q8) {
+            constexpr int NMF = 2 * G::KSTEPS8, UPM = 32 / NMF;
             i32x8 bk[G::KSTEPS8];
 #pragma unroll
             for (int s = 0; s < G::KSTEPS8; ++s) bk[s] = lds_ld32(src + 32 * s);
-            mfma_block8<D>(rows.qa, bk, acc0, acc1);
+#pragma unroll
+            for (int i = 0; i < NMF; ++i) {
+                if (i % 2 == 0)
+                    acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(rows.qa[0][i / 2], bk[i / 2], acc0, 0, 0, 0, 0, 0, 0);
+                else
+                    acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(rows.qa[1][i / 2], bk[i / 2], acc1, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < UPM; ++u) ea.unit(i * UPM + u, pa0, pa1, rows.wl);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
+            constexpr int NMF = 2 * G::KSTEPS, UPM = 32 / NMF;
             bf16x8 bk[G::KSTEPS];
 #pragma unroll
             for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
-            mfma_block<D>(rows.qa, bk, acc0, acc1);
-        }
-        const Part<H> pp = epi_reduce<H>(pa0, pa1, rows.wl, pks);
-        // shape: the B-fragment reads, then MFMAs interleaved with VALU
-        if constexpr (Q8) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G::KSTEPS8 + 1, 0);
 #pragma unroll
-            for (int i = 0; i < 2 * G::KSTEPS8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-            }
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x100, G::KSTEPS, 0);
+            for (int i = 0; i < NMF; ++i) {
+                if (i % 2 == 0)
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows.qa[0][i / 2], bk[i / 2], acc0, 0, 0, 0);
+                else
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows.qa[1][i / 2], bk[i / 2], acc1, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 2 * G::KSTEPS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                for (int u = 0; u < UPM; ++u) ea.unit(i * UPM + u, pa0, pa1, rows.wl);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // (columns past the last key are not stored: a tile may reach
-        // beyond the row stride)
-        epi_store<H>(pp, rs, pkey >= 0 && pkey < n_keys, tq0, pkey, lane);
+        sink(ea.finish(pks), pkey);
         pa0 = acc0;
         pa1 = acc1;
         pkey = key;
         pks = ksc;
     };
 
-    if constexpr (DMA) {
-        constexpr int RS = ROWB / 16;        // 16-byte slots per LDS row (row + 1 pad)
-        constexpr int NDMA = KT * RS / 64;   // 1 KB direct loads per tile (rows)
-        constexpr int MPW = (NDMA + WAVES_PREFILL - 1) / WAVES_PREFILL;
-        static_assert(KT * RS % 64 == 0, "tile must fill whole direct loads");
-        // lane l of load m fills slot 64m + l = chunk c of tile row r (pad
-        // slots re-read chunk 0); rows past the last key read as zeros
-        uint32_t goff[MPW];
-#pragma unroll
-        for (int i = 0; i < MPW; ++i) {
-            const int slot = 64 * (wave + WAVES_PREFILL * i) + lane;
-            const int row = slot / RS, c = slot - row * RS;
-            goff[i] = (uint32_t)(row * a.k_st + (c < RS - 1 ? 16 * c : 0));
-        }
-        auto gather = [&](int tile, uint8_t *dst) {
-            const int64_t key0 = (int64_t)tile * KT;
-            const int64_t rem = n_keys - key0;
-            const int nk = rem < KT ? (int)rem : KT;  // keys of this tile
-            const uint8_t *tbase = kb + key0 * a.k_st;
-            const uint32_t bytes = (uint32_t)(nk * a.k_st);
+    // Sweep over nit tiles, the i-th being tile_of(i) (tile_of(nit) must name
+    // a tile past the last key); the i-th tile's blocks carry the keys
+    // i*KT + 32*cb + lane%32.  VM is the number of global memory operations
+    // that `sink` issues per call.
+    auto sweep = [&](int nit, auto tile_of, auto &sink, auto vm) {
+        constexpr int VM = decltype(vm)::value;
+        if constexpr (DMA) {
+            constexpr int RS = ROWB / 16;        // 16-byte slots per LDS row (row + 1 pad)
+            constexpr int NDMA = KT * RS / 64;   // 1 KB direct loads per tile (rows)
+            constexpr int MPW = (NDMA + WAVES_PREFILL - 1) / WAVES_PREFILL;
+            static_assert(KT * RS % 64 == 0, "tile must fill whole direct loads");
+            // lane l of load m fills slot 64m + l = chunk c of tile row r (pad
+            // slots re-read chunk 0); rows past the last key read as zeros
+            uint32_t goff[MPW];
 #pragma unroll
             for (int i = 0; i < MPW; ++i) {
-                const int m = wave + WAVES_PREFILL * i;
-                if (m < NDMA) buffer_load_to_lds16(tbase, bytes, goff[i], dst + 1024 * m);
+                const int slot = 64 * (wave + WAVES_PREFILL * i) + lane;
+                const int row = slot / RS, c = slot - row * RS;
+                goff[i] = (uint32_t)(row * a.k_st + (c < RS - 1 ? 16 * c : 0));
             }
-            if constexpr (Q8) {
-                // the tile's KT key scales (4 per lane), by the last wave
-                if (wave == WAVES_PREFILL - 1 && lane < KT / 4)
-                    buffer_load_to_lds16(a.k_scale + b * a.ks_sb + key0, (uint32_t)(nk * 4), 16 * lane,
-                                         dst + KT * ROWB);
-            }
-        };
-        auto step = [&](int it, const uint8_t *tb, uint8_t *nb) {
-            if (it + 1 < ntiles) gather(it + 1, nb);
+            auto gather = [&](int tile, uint8_t *dst) {
+                const int64_t key0 = (int64_t)tile * KT;
+                const int64_t rem = n_keys - key0;
+                const int nk = rem < KT ? (int)rem : KT;  // keys of this tile
+                const uint8_t *tbase = kb + key0 * a.k_st;
+                const uint32_t bytes = (uint32_t)(nk * a.k_st);
 #pragma unroll
-            for (int cb = 0; cb < KT / 32; ++cb) {
-                const float ksc = Q8 ? *reinterpret_cast<const float *>(tb + KT * ROWB + 4 * (cb * 32 + l32)) : 1.f;
-                block(tb, cb, ksc, it * KT + cb * 32 + l32);
-            }
-            // this wave's loads into nb have landed (only the score stores
-            // issued after them may still be in flight), then all waves' have
-            wait_vmcnt<(KT / 32) * SPB>();
+                for (int i = 0; i < MPW; ++i) {
+                    const int m = wave + WAVES_PREFILL * i;
+                    if (m < NDMA) buffer_load_to_lds16(tbase, bytes, goff[i], dst + 1024 * m);
+                }
+                if constexpr (Q8) {
+                    // the tile's KT key scales (4 per lane), by the last wave
+                    if (wave == WAVES_PREFILL - 1 && lane < KT / 4)
+                        buffer_load_to_lds16(a.k_scale + b * a.ks_sb + key0, (uint32_t)(nk * 4), 16 * lane,
+                                             dst + KT * ROWB);
+                }
+            };
+            auto step = [&](int it, const uint8_t *tb, uint8_t *nb) {
+                if (it + 1 < nit) gather(tile_of(it + 1), nb);
+#pragma unroll
+                for (int cb = 0; cb < KT / 32; ++cb) {
+                    const float ksc = Q8 ? *reinterpret_cast<const float *>(tb + KT * ROWB + 4 * (cb * 32 + l32)) : 1.f;
+                    block(tb, cb, ksc, it * KT + cb * 32 + l32, sink);
+                }
+                // this wave's loads into nb have landed (only the sink's
+                // stores issued after them may still be in flight), then all
+                // waves' have
+                wait_vmcnt<(KT / 32) * VM>();
+                lds_barrier();
+            };
+            gather(tile_of(0), sk0);
+            wait_vmcnt<0>();
             lds_barrier();
-        };
-        gather(0, sk0);
-        wait_vmcnt<0>();
-        lds_barrier();
-        for (int it = 0; it < ntiles; it += 2) {
-            step(it, sk0, sk1);
-            if (it + 1 >= ntiles) break;
-            step(it + 1, sk1, sk0);
-        }
-    } else {
-        // 16-byte chunks of one tile as read from memory: D/16 per key
-        constexpr int SRC_CHUNK_KEY = D / 16;
-        constexpr int SRC_CHUNKS = KT * SRC_CHUNK_KEY;
-        constexpr int CPT = (SRC_CHUNKS + NT - 1) / NT;
-        u32x4 pf[CPT];
-        float pfs = 1.f;
-        // range-checked buffer loads: keys past the last one (and chunks past
-        // the tile) read as zeros without a branch, so the compiler can count
-        // the loads in flight exactly (a key's zero scale is never stored)
-        auto fetch = [&](int tile) {
-            const int64_t key0 = (int64_t)tile * KT;
-            const int64_t rem = n_keys - key0;
-            const int nk = rem <= 0 ? 0 : (rem < KT ? (int)rem : KT);  // keys of this tile (0 past the end)
-            const uint8_t *tbase = kb + key0 * a.k_st;
-            const uint32_t bytes = (uint32_t)(nk * a.k_st);
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = tid + i * NT;
-                const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
-                const uint32_t off = c < SRC_CHUNKS ? (uint32_t)(kk * a.k_st + part * 16) : bytes;
-                pf[i] = ld16_ranged(tbase, bytes, off);
+            for (int it = 0; it < nit; it += 2) {
+                step(it, sk0, sk1);
+                if (it + 1 >= nit) break;
+                step(it + 1, sk1, sk0);
             }
-            pfs = ld4_ranged(a.k_scale + b * a.ks_sb + key0, (uint32_t)(nk * 4), tid < KT ? 4 * tid : (uint32_t)(nk * 4));
-        };
-        auto stash = [&](uint8_t *dst, int buf) {
+        } else {
+            // 16-byte chunks of one tile as read from memory: D/16 per key
+            constexpr int SRC_CHUNK_KEY = D / 16;
+            constexpr int SRC_CHUNKS = KT * SRC_CHUNK_KEY;
+            constexpr int CPT = (SRC_CHUNKS + NT - 1) / NT;
+            u32x4 pf[CPT];
+            float pfs = 1.f;
+            // range-checked buffer loads: keys past the last one (and chunks
+            // past the tile) read as zeros without a branch, so the compiler
+            // can count the loads in flight exactly (a key's zero scale is
+            // never used)
+            auto fetch = [&](int tile) {
+                const int64_t key0 = (int64_t)tile * KT;
+                const int64_t rem = n_keys - key0;
+                const int nk = rem <= 0 ? 0 : (rem < KT ? (int)rem : KT);  // keys of this tile (0 past the end)
+                const uint8_t *tbase = kb + key0 * a.k_st;
+                const uint32_t bytes = (uint32_t)(nk * a.k_st);
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = tid + i * NT;
-                if (c >= SRC_CHUNKS) break;
-                const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
-                uint8_t *row = dst + kk * ROWB;
-                // 16 fp8 bytes -> 16 bf16 (32 bytes)
-                u32x2 lo0 = fp8x4_to_bf16x4(pf[i].x), lo1 = fp8x4_to_bf16x4(pf[i].y);
-                u32x2 hi0 = fp8x4_to_bf16x4(pf[i].z), hi1 = fp8x4_to_bf16x4(pf[i].w);
-                st16(row + part * 32, u32x4{lo0.x, lo0.y, lo1.x, lo1.y});
-                st16(row + part * 32 + 16, u32x4{hi0.x, hi0.y, hi1.x, hi1.y});
-            }
-            if (tid < KT) ssc[buf][tid] = pfs;
-        };
-        fetch(0);
-        stash(sk0, 0);
-        __syncthreads();
-        // (the tile after the last is fetched and stashed too -- as zeros,
-        // into the buffer nobody reads any more -- so the loop body has no
-        // branch around its loads and the compiler's wait counts stay exact)
-        for (int it = 0; it < ntiles; ++it) {
-            const int buf = it & 1;
-            fetch(it + 1);
+                for (int i = 0; i < CPT; ++i) {
+                    const int c = tid + i * NT;
+                    const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
+                    const uint32_t off = c < SRC_CHUNKS ? (uint32_t)(kk * a.k_st + part * 16) : bytes;
+                    pf[i] = ld16_ranged(tbase, bytes, off);
+                }
+                pfs = ld4_ranged(a.k_scale + b * a.ks_sb + key0, (uint32_t)(nk * 4), tid < KT ? 4 * tid : (uint32_t)(nk * 4));
+            };
+            auto stash = [&](uint8_t *dst, int buf) {
 #pragma unroll
-            for (int cb = 0; cb < KT / 32; ++cb)
-                block(buf ? sk1 : sk0, cb, ssc[buf][cb * 32 + l32], it * KT + cb * 32 + l32);
-            stash(buf ? sk0 : sk1, buf ^ 1);
+                for (int i = 0; i < CPT; ++i) {
+                    const int c = tid + i * NT;
+                    if (c >= SRC_CHUNKS) break;
+                    const int kk = c / SRC_CHUNK_KEY, part = c % SRC_CHUNK_KEY;
+                    uint8_t *row = dst + kk * ROWB;
+                    // 16 fp8 bytes -> 16 bf16 (32 bytes)
+                    u32x2 lo0 = fp8x4_to_bf16x4(pf[i].x), lo1 = fp8x4_to_bf16x4(pf[i].y);
+                    u32x2 hi0 = fp8x4_to_bf16x4(pf[i].z), hi1 = fp8x4_to_bf16x4(pf[i].w);
+                    st16(row + part * 32, u32x4{lo0.x, lo0.y, lo1.x, lo1.y});
+                    st16(row + part * 32 + 16, u32x4{hi0.x, hi0.y, hi1.x, hi1.y});
+                }
+                if (tid < KT) ssc[buf][tid] = pfs;
+            };
+            fetch(tile_of(0));
+            stash(sk0, 0);
             __syncthreads();
+            // (the tile after the last is fetched and stashed too -- as
+            // zeros, into the buffer nobody reads any more -- so the loop body
+            // has no branch around its loads and the compiler's wait counts
+            // stay exact)
+            for (int it = 0; it < nit; ++it) {
+                const int buf = it & 1;
+                fetch(tile_of(it + 1));
+#pragma unroll
+                for (int cb = 0; cb < KT / 32; ++cb)
+                    block(buf ? sk1 : sk0, cb, ssc[buf][cb * 32 + l32], it * KT + cb * 32 + l32, sink);
+                stash(buf ? sk0 : sk1, buf ^ 1);
+                __syncthreads();
+            }
+        }
+        sink(epi_reduce<H>(pa0, pa1, rows.wl, pks), pkey);
+        pkey = -1;
+    };
+    auto all_tiles = [](int i) { return i; };
+
+    if constexpr (!FUSE) {
+        // (columns past the last key are not stored: a tile may reach
+        // beyond the row stride)
+        auto store_sink = [&](const Part<H> &pp, int key) {
+            epi_store<H>(pp, rs, key >= 0 && key < n_keys, tq0, key, lane);
+        };
+        sweep(ntiles, all_tiles, store_sink, std::integral_constant<int, SPB>{});
+    } else {
+        // the lanes holding query q's reduced scores (one half of the wave)
+        auto mine = [&](int q) { return QPW == 1 ? g == 0 : (q < QPW / 2) == (g == 0); };
+        float tau[QPW];
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) tau[q] = -__builtin_inff();
+        if (n_keys > FUSE_CAP) {
+            const int nts = (int)((a.q_pos0 + t0 + 1) / KT);  // whole tiles below every row's position
+            auto sample_tiles = [&](int i) { return i < NS ? (int)((int64_t)i * nts / NS) : ntiles; };
+            auto sample_sink = [&](const Part<H> &pp, int key) {
+                if (key < 0) return;
+#pragma unroll
+                for (int q = 0; q < QPW; ++q)
+                    if (mine(q)) samp[(wave * QPW + q) * SPQ + key] = pp.v[q];
+            };
+            sweep(NS, sample_tiles, sample_sink, std::integral_constant<int, 0>{});
+            // each wave reads only the samples it wrote
+#pragma unroll
+            for (int q = 0; q < QPW; ++q) {
+                if (tq0 + q >= a.T_q) break;
+                const float n = (float)(a.q_pos0 + tq0 + q + 1);
+                const float mu = (float)SPQ * (float)a.top_k / n;
+                float r = ceilf(mu + 4.5f * sqrtf(mu) + 2.f);
+                r = fminf(fmaxf(r, 1.f), (float)SPQ);
+                tau[q] = sample_threshold<SPQ>(samp + (wave * QPW + q) * SPQ, (int)r, lane);
+            }
+        }
+        constexpr uint32_t CAPB = FUSE_CAP * 8;
+        uint32_t plim[QPW];
+        int cnt[QPW];
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) {
+            // the row's last causal key (as unsigned, the key -1 before the
+            // first block lies above it); rows past T_q pass nothing
+            const bool row_ok = tq0 + q < a.T_q;
+            plim[q] = row_ok ? (uint32_t)(a.q_pos0 + tq0 + q) : 0u;
+            if (!row_ok) tau[q] = __builtin_inff();
+            cnt[q] = 0;
+        }
+        auto filter_sink = [&](const Part<H> &pp, int key) {
+#pragma unroll
+            for (int q = 0; q < QPW; ++q) {
+                // (bitwise ands: no short-circuit branches in the loop)
+                const bool pass = mine(q) & ((uint32_t)key <= plim[q]) & (pp.v[q] >= tau[q]);
+                const uint64_t m = ballot(pass);
+                const uint32_t off = pass ? (uint32_t)(cnt[q] + lanes_below(m)) * 8u : CAPB;
+                uint32_t *base = a.cand + ((int64_t)b * a.T_q + tq0 + q) * (2 * FUSE_CAP);
+                store_b64_ranged(base, CAPB, off, u32x2{__float_as_uint(pp.v[q]), (uint32_t)key});
+                cnt[q] = min(cnt[q] + (int)__popcll(m), FUSE_CAP + 1);  // saturates past the slots
+            }
+        };
+        sweep(ntiles, all_tiles, filter_sink, std::integral_constant<int, SPB>{});
+        if (lane == 0) {
+#pragma unroll
+            for (int q = 0; q < QPW; ++q)
+                if (tq0 + q < a.T_q) a.ccnt[(int64_t)b * a.T_q + tq0 + q] = cnt[q];
         }
     }
-    epi_store<H>(epi_reduce<H>(pa0, pa1, rows.wl, pks), rs, pkey >= 0 && pkey < n_keys, tq0, pkey, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,8 +740,16 @@ hipError_t launch_score_hd(const ScoreArgs &a, bool split, hipStream_t st)
     if (!split) {
         constexpr int QPB = WAVES_PREFILL * QPW;
         dim3 grid((a.T_q + QPB - 1) / QPB, a.B);
-        hipLaunchKernelGGL((score_prefill_kernel<H, D, F>), grid, dim3(WAVES_PREFILL * 64), 0, st, a);
+        if constexpr (H >= 16) {
+            if (a.fuse) {
+                hipLaunchKernelGGL((score_prefill_kernel<H, D, F, true>), grid, dim3(WAVES_PREFILL * 64), 0, st, a);
+                return hipGetLastError();
+            }
+        }
+        if (a.fuse) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((score_prefill_kernel<H, D, F, false>), grid, dim3(WAVES_PREFILL * 64), 0, st, a);
     } else {
+        if (a.fuse || a.redo) return hipErrorInvalidValue;
         const int64_t n_keys = a.q_pos0 + a.T_q;
         dim3 grid((unsigned)((n_keys + a.key_split - 1) / a.key_split), (a.T_q + QPW - 1) / QPW, a.B);
         hipLaunchKernelGGL((score_splitkey_kernel<H, D, F>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
@@ -607,6 +781,11 @@ bool score_use_split(const ScoreArgs &a)
     const int qpb = WAVES_PREFILL * (64 / a.H);
     const int64_t blocks = (int64_t)a.B * ((a.T_q + qpb - 1) / qpb);
     return blocks < 256 && (a.q_pos0 + a.T_q) >= 4096;
+}
+
+bool score_can_fuse(const ScoreArgs &a)
+{
+    return a.H >= 16 && !score_use_split(a) && a.q_pos0 + a.T_q > a.top_k;
 }
 
 int score_key_split(const ScoreArgs &a)

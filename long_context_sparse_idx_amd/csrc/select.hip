@@ -13,7 +13,9 @@
 // to K* are taken; a stable, wave-ordered compaction then writes every entry
 // with key > K* and the first `need` entries with key == K*.
 //
-// One 512-thread workgroup per row, three paths:
+// One 512-thread workgroup per row, three paths (after a fused score pass,
+// rows whose candidate count is usable select from their candidates
+// instead):
 //  A  n <= 16384: the whole row's keys sit in LDS; select there.
 //  B  longer rows: 8192 sampled scores (32 evenly spaced runs of 256) give
 //     a threshold tau expected to pass ~2.5k entries; one streaming pass
@@ -99,6 +101,17 @@ struct GlobalRow {
             if (i + 2 < n) f(order_key(v.z));
             if (i + 3 < n) f(order_key(v.w));
         }
+    }
+};
+
+// Candidates of a fused score pass: (score bits, position) pairs in
+// ascending position order.
+struct GlobalPairs {
+    const uint32_t *p;
+    int n;
+    template <class F> __device__ void visit(F f) const
+    {
+        for (int i = threadIdx.x; i < n; i += NT) f(order_key(__uint_as_float(p[2 * i])));
     }
 };
 
@@ -296,6 +309,57 @@ struct GlobalSeg {
     }
 };
 
+struct GlobalPairSeg {
+    const uint32_t *p;
+    int n, seg;
+    __device__ int len(int w) const { return seg; }
+    __device__ bool get(int w, int j, uint32_t &key, int32_t &pos) const
+    {
+        const int i = w * seg + j;
+        if (j >= seg || i >= n) return false;
+        const u32x2 e = *reinterpret_cast<const u32x2 *>(p + 2 * i);
+        key = order_key(__uint_as_float(e.x));
+        pos = (int32_t)e.y;
+        return true;
+    }
+};
+
+// Exact top-k of a row from the c >= k candidates of a fused score pass
+// (every score at or above the row's k-th largest is among them): in the
+// per-wave LDS lists when they fit, as an LDS row when the candidates are
+// the whole row (n <= NLDS), else streaming the pairs from memory.
+__device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t n, int32_t *out, int k)
+{
+    const int tid = threadIdx.x;
+    if (c <= NW * CAPW) {
+        // cut into NW consecutive parts, one per wave list, so the lists
+        // visited wave by wave stay ascending
+        const int per = (c + NW - 1) / NW;
+        for (int i = tid; i < c; i += NT) {
+            const u32x2 e = *reinterpret_cast<const u32x2 *>(cp + 2 * i);
+            const int v = i / per, j = i - v * per;
+            sh.u.cand.key[v * CAPW + j] = order_key(__uint_as_float(e.x));
+            sh.u.cand.idx[v * CAPW + j] = (int32_t)e.y;
+        }
+        if (tid < NW) sh.wcnt[tid] = max(0, min(per, c - tid * per));
+        __syncthreads();
+        radix_find(sh, Candidates{&sh}, k);
+        emit(sh, CandSeg{&sh}, out, k);
+        return;
+    }
+    const int seg = ((c + NW - 1) / NW + 63) / 64 * 64;
+    if (c == n && n <= NLDS) {
+        // every score passed: the candidates are the row, positions 0 .. n-1
+        for (int i = tid; i < c; i += NT) sh.u.keys[i] = order_key(__uint_as_float(cp[2 * i]));
+        __syncthreads();
+        radix_find(sh, LdsKeys{sh.u.keys, c}, k);
+        emit(sh, LdsSeg{&sh, c, seg}, out, k);
+        return;
+    }
+    radix_find(sh, GlobalPairs{cp, c}, k);
+    emit(sh, GlobalPairSeg{cp, c, seg}, out, k);
+}
+
 // Threshold for the sampled pass over a row of n > NLDS scores: 8192 scores
 // in 32 evenly spaced runs of 256 give the key tau that about 2.5k entries
 // of the row are expected to reach.  Every thread returns tau.
@@ -384,6 +448,16 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     if (n <= k) {
         for (int j = tid; j < m; j += NT) out[j] = j;
         return;
+    }
+    if (a.cand) {
+        // after a fused score pass: the row's candidates, unless their count
+        // says the row was rescored in full
+        const int64_t r = (int64_t)b * a.T_q + t;
+        const int c = a.ccnt[r];
+        if (!fused_row_bad(c, n, k)) {
+            select_from_pairs(sh, a.cand + r * (2 * FUSE_CAP), c, n, out, k);
+            return;
+        }
     }
 
     if (n <= NLDS) {
@@ -567,7 +641,7 @@ size_t select_ws_bytes(int B, int T_q, int64_t q_pos0)
 hipError_t launch_select(const SelectArgs &a_in, void *extra, hipStream_t st)
 {
     const MultiPlan p = multi_plan(a_in.B, a_in.T_q, a_in.q_pos0);
-    if (!p.on) {
+    if (!p.on || a_in.cand) {
         hipLaunchKernelGGL(select_kernel, dim3(a_in.T_q, a_in.B), dim3(NT), 0, st, a_in);
         return hipGetLastError();
     }

@@ -30,6 +30,7 @@ LCSI_Q_BF16 = 0
 LCSI_Q_FP8_E4M3 = 1
 LCSI_SCORES_PRESET = 1
 LCSI_SCORES_ONLY = 2
+LCSI_UNFUSED = 4
 LCSI_MAX_TOPK = 2048
 
 EXPORTED = ("idx_score_topk", "sparse_attn", "run_layer_group", "idx_overlap", "lcsi_score_ld", "lcsi_strerror")

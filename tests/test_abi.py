@@ -79,9 +79,20 @@ def call_idx(d, idx=FAKE, ws=None, nbytes=None, flags=0, sb=16 * 8, st=8):
 
 
 def test_indexer_query_mode_returns_workspace_size():
+    rows_bytes = 2 * 16 * lcsi.score_ld(100) * 4
+    # default: the fused pass (H_I >= 16, prefill kernel, rows longer than
+    # top_k) adds 256-aligned counts and 16384 candidate pairs per row
     rc, n = call_idx(good_indexer())
     assert rc == 0
-    assert n == 2 * 16 * lcsi.score_ld(100) * 4
+    assert n == rows_bytes + 256 + 2 * 16 * 16384 * 8
+    for flags in (lcsi.LCSI_UNFUSED, lcsi.LCSI_SCORES_ONLY, lcsi.LCSI_SCORES_PRESET):
+        rc, n = call_idx(good_indexer(), flags=flags)
+        assert rc == 0 and n == rows_bytes, flags
+    # no fused pass below 16 heads, nor when no row is longer than top_k
+    rc, n = call_idx(good_indexer(H_I=8, q_sh=128, w_sb=16 * 8, w_st=8))
+    assert rc == 0 and n == rows_bytes
+    rc, n = call_idx(good_indexer(top_k=100))
+    assert rc == 0 and n == rows_bytes
     rc, n = call_idx(good_indexer(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE, ks_sb=100,
                                   k_sb=100 * 128, k_st=128))
     assert rc == 0 and n > 0

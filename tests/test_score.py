@@ -23,14 +23,21 @@ pytestmark = pytest.mark.gpu
 
 
 def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None, q_scale=None):
-    """Returns (scores [B, T_q, ld] float32 host, idx [B, T_q, k] host)."""
+    """Returns (scores [B, T_q, ld] float32 host, idx [B, T_q, k] host).
+
+    idx comes from the default call (the fused candidate pass wherever it
+    applies) and must equal, bit for bit, the indices of the unfused call
+    (every score row written, then selected), whose rows are the scores."""
     B, T_q = q.shape[:2]
     T_kv = k.shape[1]
     d = lcsi.indexer_desc(q, k, w, top_k, q_pos0, k_scale=k_scale, q_scale=q_scale)
     ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4, dtype=torch.float32, device="cuda")
     idx = torch.empty((B, T_q, top_k), dtype=torch.int32, device="cuda")
+    idx_u = torch.empty_like(idx)
     lcsi.idx_score_topk(d, idx, ws)
+    lcsi.idx_score_topk(d, idx_u, ws, flags=lcsi.LCSI_UNFUSED)
     torch.cuda.synchronize()
+    assert torch.equal(idx, idx_u), "fused and unfused indices differ"
     ld = lcsi.score_ld(T_kv)
     return ws[:B * T_q * ld].view(B, T_q, ld).cpu().numpy(), idx.cpu().numpy()
 
