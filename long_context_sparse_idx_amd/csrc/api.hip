@@ -107,7 +107,7 @@ size_t score_ws_bytes(const lcsi_indexer *a, unsigned flags)
     size_t s = score_rows_bytes(a) + select_ws_bytes(a->B, a->T_q, a->q_pos0);
     if (fused_plan(a, flags)) {
         const size_t rows = (size_t)a->B * (size_t)a->T_q;
-        s += align_ws(rows * 4) + rows * FUSE_CAP * 8;
+        s += align_ws(rows * 4) + align_ws((1 + FUSE_RMAX) * 4) + rows * FUSE_CAP * 8;
     }
     return s;
 }
@@ -196,14 +196,29 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
         sa.key_split = score_key_split(sa);
         sa.top_k = a->top_k;
         if (fused) {
+            // workspace past the rows: counts, the list of unsettled rows
+            // (its length first), candidate slots
             uint8_t *fz = (uint8_t *)ws + score_rows_bytes(a) + select_ws_bytes(a->B, a->T_q, a->q_pos0);
             sa.ccnt = (int32_t *)fz;
-            sa.cand = (uint32_t *)(fz + align_ws((size_t)a->B * a->T_q * 4));
+            fz += align_ws((size_t)a->B * a->T_q * 4);
+            sa.rcount = (int32_t *)fz;
+            sa.rlist = sa.rcount + 1;
+            sa.rmax = FUSE_RMAX;
+            sa.cand = (uint32_t *)(fz + align_ws((1 + FUSE_RMAX) * 4));
+            if (launch_zero_i32(sa.rcount, s) != hipSuccess) return LCSI_EHIP;
             sa.fuse = 1;
             if (launch_score(sa, s) != hipSuccess) return LCSI_EHIP;
-            // full rows for the workgroups holding a row the candidates
-            // cannot settle (usually none: then every workgroup exits at once)
+            // full rows for the rows the candidates cannot settle (usually
+            // none: then every workgroup exits at once): listed rows by the
+            // split-key kernel, 64 key ranges each ...
             sa.fuse = 0;
+            const int64_t n_keys = a->q_pos0 + a->T_q;
+            int64_t ks = (n_keys + 63) / 64;
+            ks = (ks + 255) / 256 * 256;
+            sa.key_split = score_key_range(ks < 512 ? 512 : ks, sa.k_st);
+            if (launch_score(sa, s) != hipSuccess) return LCSI_EHIP;
+            // ... and, if the list overflowed, the workgroups holding such rows
+            sa.rlist = nullptr;
             sa.redo = sa.ccnt;
             if (launch_score(sa, s) != hipSuccess) return LCSI_EHIP;
             cand = sa.cand;

@@ -37,6 +37,14 @@ struct ScoreArgs {
     // workgroup runs only if one of its rows has a count the selection
     // cannot use (fused_row_bad), and then writes its full rows to S
     const int32_t *redo;      // [B * T_q] counts of the fused pass, or null
+    // rows the fused pass could not settle: it appends their ids (b*T_q + t)
+    // to rlist (the first rmax of them; *rcount counts them all, and must be
+    // zero before the pass).  The split-key kernel with rlist set rescores
+    // listed rows (blockIdx.y = list entry); the prefill kernel with redo set
+    // runs only when the list overflowed.
+    int32_t *rlist;           // [rmax]
+    int32_t *rcount;
+    int rmax;
 };
 
 // Candidate slots per row of the fused selection.
@@ -94,7 +102,15 @@ bool score_use_split(const ScoreArgs &a);
 // Whether a call with these arguments can take the fused selection.
 bool score_can_fuse(const ScoreArgs &a);
 int score_key_split(const ScoreArgs &a);
+// ks keys per split-key workgroup, lowered to what 32-bit byte offsets reach
+// at a key stride of k_st_bytes.
+int score_key_range(int64_t ks, int64_t k_st_bytes);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
+// Zero one int32 in device memory (a kernel, so the call may be captured
+// in a graph).
+hipError_t launch_zero_i32(int32_t *p, hipStream_t st);
+// Rows a rescoring launch takes from the fused pass's list.
+constexpr int FUSE_RMAX = 64;
 // Workspace bytes the selection needs past the score rows (0 unless few
 // long rows take the multi-workgroup path), and the launch (extra = that
 // part of the workspace).

@@ -299,8 +299,9 @@ __device__ __forceinline__ void mfma_block8(const i32x8 (&qa)[2][KeyGeom<D>::KST
 // Fused selection (FUSE, H >= 16): instead of the score row, the kernel
 // writes each row's candidates for the top-k.
 //   1. Sample: when the workgroup's longest row has more than FUSE_CAP keys,
-//      it first scores NS whole tiles spread evenly over the keys that all
-//      its rows cover (SPQ keys per query row) into LDS, and each wave takes,
+//      it first scores ns whole tiles spread evenly over the keys that all
+//      its rows cover into LDS (ns: enough for about 24 sampled scores above
+//      a row's k-th largest, between 4 and NS = SPQ / KT), and each wave takes,
 //      for each of its query rows, the r-th largest sampled score as the
 //      row's threshold tau.  r is the expected number of sampled scores at
 //      or above the row's k-th largest, plus 4.5 standard deviations and 2,
@@ -316,26 +317,39 @@ __device__ __forceinline__ void mfma_block8(const i32x8 (&qa)[2][KeyGeom<D>::KST
 // the row.  A count below k or above FUSE_CAP only costs time: the caller
 // rescores those rows in full (fused_row_bad).
 // ---------------------------------------------------------------------------
-constexpr int FUSE_SAMPLES = 16384;  // sampled scores per workgroup (64 KB of LDS)
+constexpr int FUSE_SAMPLES = 32768;  // sampled scores per workgroup, 16 bits each (64 KB of LDS)
+
+// Sampled scores are kept as their upper 16 bits (a float truncated toward
+// zero: monotone, so order statistics of the truncated values bound those
+// of the scores closely; the threshold only steers the candidate count, the
+// count decides whether the candidates are used).  ok16: the 16-bit
+// order-preserving key of such a value (-0 folded onto +0).
+__device__ __forceinline__ uint32_t ok16(uint32_t h)
+{
+    if (h == 0x8000u) h = 0u;
+    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
 
 template <int SPQ>
-__device__ __forceinline__ float sample_threshold(const float *s, int r, int lane)
+__device__ __forceinline__ float sample_threshold(const uint16_t *s, int ns, int r, int lane)
 {
-    // the r-th largest of the SPQ sampled keys, bit by bit from the top: the
-    // largest key T that at least r samples reach
+    // the r-th largest of the ns (<= SPQ) sampled keys, bit by bit from the
+    // top: the largest key T that at least r samples reach (unused slots
+    // count as key 0, below every candidate T)
     uint32_t kk[SPQ / 64];
 #pragma unroll
-    for (int j = 0; j < SPQ / 64; ++j) kk[j] = order_key(s[64 * j + lane]);
+    for (int j = 0; j < SPQ / 64; ++j) kk[j] = 64 * j + lane < ns ? ok16(s[64 * j + lane]) : 0u;
     uint32_t T = 0;
 #pragma unroll 1
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 15; bit >= 0; --bit) {
         const uint32_t c = T | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < SPQ / 64; ++j) cnt += __popcll(ballot(kk[j] >= c));
         if (cnt >= r) T = c;
     }
-    return __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
+    const uint32_t h = (T & 0x8000u) ? (T & 0x7FFFu) : (~T & 0xFFFFu);
+    return __uint_as_float(h << 16);
 }
 
 template <int H, int D, int F, bool FUSE>
@@ -358,7 +372,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     __shared__ __attribute__((aligned(1024))) uint8_t sk0[KT * ROWB + SCB];
     __shared__ __attribute__((aligned(1024))) uint8_t sk1[KT * ROWB + SCB];
     __shared__ float ssc[2][F == F_K8 ? KT : 1];
-    __shared__ float samp[FUSE ? FUSE_SAMPLES : 1];
+    __shared__ uint16_t samp[FUSE ? FUSE_SAMPLES : 1];
 
     // (the wave index as a scalar: addresses built from it, such as a
     // buffer resource, are then known to be the same in every lane)
@@ -372,9 +386,10 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     const uint8_t *kb = a.k + b * a.k_sb;
 
     if constexpr (!FUSE) {
-        // rescoring after a fused pass: only workgroups holding a row whose
-        // candidates the selection cannot use
+        // rescoring after a fused pass, when its list of unsettled rows
+        // overflowed: only workgroups holding such a row
         if (a.redo) {
+            if (*a.rcount <= a.rmax) return;
             bool any = false;
             for (int t = t0; t < t_end; ++t)
                 any |= fused_row_bad(a.redo[(int64_t)b * a.T_q + t], a.q_pos0 + t + 1, a.top_k);
@@ -561,6 +576,8 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         }
         sink(epi_reduce<H>(pa0, pa1, rows.wl, pks), pkey);
         pkey = -1;
+        pa0 = f32x16{0};
+        pa1 = f32x16{0};
     };
     auto all_tiles = [](int i) { return i; };
 
@@ -578,24 +595,30 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
 #pragma unroll
         for (int q = 0; q < QPW; ++q) tau[q] = -__builtin_inff();
         if (n_keys > FUSE_CAP) {
-            const int nts = (int)((a.q_pos0 + t0 + 1) / KT);  // whole tiles below every row's position
-            auto sample_tiles = [&](int i) { return i < NS ? (int)((int64_t)i * nts / NS) : ntiles; };
+            const int64_t n_min = a.q_pos0 + t0 + 1;
+            const int nts = (int)(n_min / KT);  // whole tiles below every row's position
+            // sampled tiles: enough for about 24 sampled scores at or above
+            // each row's k-th largest, at least 4, at most NS (the LDS share)
+            const int64_t want = (24 * n_min + (int64_t)a.top_k * KT - 1) / ((int64_t)a.top_k * KT);
+            const int ns = (int)(want < 4 ? 4 : (want > NS ? NS : want));
+            auto sample_tiles = [&](int i) { return i < ns ? (int)((int64_t)i * nts / ns) : ntiles; };
             auto sample_sink = [&](const Part<H> &pp, int key) {
                 if (key < 0) return;
 #pragma unroll
                 for (int q = 0; q < QPW; ++q)
-                    if (mine(q)) samp[(wave * QPW + q) * SPQ + key] = pp.v[q];
+                    if (mine(q)) samp[(wave * QPW + q) * SPQ + key] = (uint16_t)(__float_as_uint(pp.v[q]) >> 16);
             };
-            sweep(NS, sample_tiles, sample_sink, std::integral_constant<int, 0>{});
+            sweep(ns, sample_tiles, sample_sink, std::integral_constant<int, 0>{});
             // each wave reads only the samples it wrote
+            const int nsk = ns * KT;  // sampled keys per row
 #pragma unroll
             for (int q = 0; q < QPW; ++q) {
                 if (tq0 + q >= a.T_q) break;
                 const float n = (float)(a.q_pos0 + tq0 + q + 1);
-                const float mu = (float)SPQ * (float)a.top_k / n;
+                const float mu = (float)nsk * (float)a.top_k / n;
                 float r = ceilf(mu + 4.5f * sqrtf(mu) + 2.f);
-                r = fminf(fmaxf(r, 1.f), (float)SPQ);
-                tau[q] = sample_threshold<SPQ>(samp + (wave * QPW + q) * SPQ, (int)r, lane);
+                r = fminf(fmaxf(r, 1.f), (float)nsk);
+                tau[q] = sample_threshold<SPQ>(samp + (wave * QPW + q) * SPQ, nsk, (int)r, lane);
             }
         }
         constexpr uint32_t CAPB = FUSE_CAP * 8;
@@ -625,8 +648,16 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         sweep(ntiles, all_tiles, filter_sink, std::integral_constant<int, SPB>{});
         if (lane == 0) {
 #pragma unroll
-            for (int q = 0; q < QPW; ++q)
-                if (tq0 + q < a.T_q) a.ccnt[(int64_t)b * a.T_q + tq0 + q] = cnt[q];
+            for (int q = 0; q < QPW; ++q) {
+                const int t = tq0 + q;
+                if (t >= a.T_q) break;
+                const int32_t id = b * a.T_q + t;
+                a.ccnt[id] = cnt[q];
+                if (fused_row_bad(cnt[q], a.q_pos0 + t + 1, a.top_k)) {
+                    const int slot = atomicAdd(a.rcount, 1);
+                    if (slot < a.rmax) a.rlist[slot] = id;
+                }
+            }
         }
     }
 }
@@ -648,8 +679,16 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     constexpr int NLD = K8 ? G::HALF / 16 : G::HALF / 8;  // 16-byte loads per lane per block
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-    const int b = blockIdx.z;
-    const int tq0 = blockIdx.y * QPW;
+    int b = blockIdx.z;
+    int tq0 = blockIdx.y * QPW;
+    if (a.rlist) {
+        // rescoring listed rows: entry blockIdx.y names the row (its group)
+        if ((int)blockIdx.y >= min(*a.rcount, a.rmax)) return;
+        const int id = a.rlist[blockIdx.y];
+        b = id / a.T_q;
+        const int t = id - b * a.T_q;
+        tq0 = t - t % QPW;
+    }
     const int64_t n_keys = a.q_pos0 + min(a.T_q, tq0 + QPW);
     const int64_t key_lo = (int64_t)blockIdx.x * a.key_split;
     const int64_t key_hi = min<int64_t>(n_keys, key_lo + a.key_split);
@@ -752,6 +791,7 @@ hipError_t launch_score_hd(const ScoreArgs &a, bool split, hipStream_t st)
         if (a.fuse || a.redo) return hipErrorInvalidValue;
         const int64_t n_keys = a.q_pos0 + a.T_q;
         dim3 grid((unsigned)((n_keys + a.key_split - 1) / a.key_split), (a.T_q + QPW - 1) / QPW, a.B);
+        if (a.rlist) grid = dim3(grid.x, a.rmax, 1);
         hipLaunchKernelGGL((score_splitkey_kernel<H, D, F>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
     }
     return hipGetLastError();
@@ -788,21 +828,40 @@ bool score_can_fuse(const ScoreArgs &a)
     return a.H >= 16 && !score_use_split(a) && a.q_pos0 + a.T_q > a.top_k;
 }
 
+int score_key_range(int64_t ks, int64_t k_st_bytes)
+{
+    // the keys of one workgroup are read through a buffer resource with
+    // 32-bit offsets: at most 2^31 - 1 bytes (a multiple of 32 keys; the
+    // key stride is below 16 MiB, so at least 128 keys)
+    const int64_t lim = ((((int64_t)1 << 31) - 1) / (k_st_bytes > 0 ? k_st_bytes : 1)) / 32 * 32;
+    return (int)(ks < lim ? ks : lim);
+}
+
 int score_key_split(const ScoreArgs &a)
 {
-    // aim for >= ~1024 workgroups; keep ranges a multiple of 32 keys
+    // aim for >= ~1024 workgroups; keep ranges a multiple of 256 keys
     const int64_t n_keys = a.q_pos0 + a.T_q;
     const int64_t groups = (int64_t)a.B * ((a.T_q + 64 / a.H - 1) / (64 / a.H));
     int64_t splits = (1024 + groups - 1) / groups;
     int64_t ks = (n_keys + splits - 1) / splits;
     ks = ((ks + 255) / 256) * 256;
     if (ks < 512) ks = 512;
-    return (int)ks;
+    return score_key_range(ks, a.k_st);
+}
+
+namespace {
+__global__ void zero_i32_kernel(int32_t *p) { *p = 0; }
+}  // namespace
+
+hipError_t launch_zero_i32(int32_t *p, hipStream_t st)
+{
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, st, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st)
 {
-    const bool split = score_use_split(a);
+    const bool split = a.rlist && !a.fuse ? true : score_use_split(a);
     switch (a.H) {
     case 4: return launch_score_h<4>(a, split, st);
     case 8: return launch_score_h<8>(a, split, st);

@@ -81,10 +81,11 @@ def call_idx(d, idx=FAKE, ws=None, nbytes=None, flags=0, sb=16 * 8, st=8):
 def test_indexer_query_mode_returns_workspace_size():
     rows_bytes = 2 * 16 * lcsi.score_ld(100) * 4
     # default: the fused pass (H_I >= 16, prefill kernel, rows longer than
-    # top_k) adds 256-aligned counts and 16384 candidate pairs per row
+    # top_k) adds 256-aligned counts, the 256-aligned list of unsettled rows
+    # (a count and 64 row ids) and 16384 candidate pairs per row
     rc, n = call_idx(good_indexer())
     assert rc == 0
-    assert n == rows_bytes + 256 + 2 * 16 * 16384 * 8
+    assert n == rows_bytes + 256 + 512 + 2 * 16 * 16384 * 8
     for flags in (lcsi.LCSI_UNFUSED, lcsi.LCSI_SCORES_ONLY, lcsi.LCSI_SCORES_PRESET):
         rc, n = call_idx(good_indexer(), flags=flags)
         assert rc == 0 and n == rows_bytes, flags

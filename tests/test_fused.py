@@ -12,9 +12,12 @@ made large exactly on the sampled tiles: the threshold lands above the
 row's k-th score).  Long rows with few sampled scores per row (16 heads)
 cover candidate counts above what the LDS lists hold.
 
-The counts are read back from the workspace (after the score rows: the
-256-aligned counts, then 16384 (score, position) pairs per row) to check
-that each case took the path it is meant to."""
+Unsettled rows are listed by the fused pass; the first 64 are rescored by
+the split-key kernel (many workgroups per row), and only when the list
+overflows do whole workgroups rescore their rows.  Both are covered.
+
+The counts are read back from the workspace (right after the score rows) to
+check that each case took the path it is meant to."""
 import numpy as np
 import pytest
 import torch
@@ -26,7 +29,7 @@ from helpers import bits, log
 pytestmark = pytest.mark.gpu
 
 CAP = 16384          # candidate slots per row
-SAMPLES = 16384      # sampled scores per workgroup (8 waves x 64/H rows)
+RMAX = 64            # unsettled rows a rescoring launch takes from the list
 
 
 def run_both(d, B, T_q, k):
@@ -144,47 +147,51 @@ def test_fused_all_ties_overflow_and_rescore():
     assert (idx == np.arange(k, dtype=np.int32)[None, None, :]).all()
 
 
-def test_fused_threshold_too_high_rescore():
-    """Keys scaled up exactly on the tiles the fused pass samples: the
-    sampled threshold lands above every row's k-th score, the row keeps
-    fewer than k candidates and is rescored.  One workgroup per batch entry
-    (8 rows), 256 entries, so every workgroup samples the same tiles: the
-    whole tiles below its first row's position, 16 of 128 keys spread
-    evenly (tile i * n_tiles // 16)."""
+@pytest.mark.parametrize("n_hot", [4, 64])
+def test_fused_threshold_too_high_rescore(n_hot):
+    """Keys scaled up exactly on the tiles the fused pass samples, in the
+    first n_hot batch entries: the sampled threshold lands above each of
+    their rows' k-th score, the rows keep fewer than k candidates and are
+    rescored -- 32 rows: from the list of unsettled rows, by the split-key
+    kernel; 512 rows: more than the list holds, by whole workgroups.  One
+    workgroup per batch entry (8 rows), 256 entries: of the n_tiles whole
+    128-key tiles below the first row's position, a workgroup samples ns
+    spread evenly (tile i * n_tiles // ns), ns = ceil(24 n / (k 128))
+    clamped to 4..32 (about 24 sampled scores above the k-th)."""
     B, H, D, k = 256, 64, 128, 2048
     T_q, q_pos0 = 8, 20000
     T_kv = q_pos0 + T_q
     g = torch.Generator().manual_seed(12)
-    q = torch.randint(-8, 9, (B, T_q, H, D), generator=g).to(torch.float32)
-    kk = torch.randint(-8, 9, (1, T_kv, D), generator=g).to(torch.float32)
+    qd = torch.randint(-8, 9, (B, T_q, H, D), generator=g, dtype=torch.int8).to(torch.bfloat16)
+    kd = torch.randint(-8, 9, (B, T_kv, D), generator=g, dtype=torch.int8).to(torch.bfloat16)
     n_tiles = (q_pos0 + 1) // 128
-    for i in range(16):
-        t = i * n_tiles // 16
-        kk[:, t * 128:(t + 1) * 128] *= 16
+    ns = min(32, max(4, -(-24 * (q_pos0 + 1) // (k * 128))))
+    for i in range(ns):
+        t = i * n_tiles // ns
+        kd[:n_hot, t * 128:(t + 1) * 128] *= 16  # integers up to 128: exact in bf16
     w = torch.ones((B, T_q, H))
-    qd, kd = q.to(torch.bfloat16), kk.to(torch.bfloat16)
-    # every batch entry reads the same keys (batch stride 0)
-    dq, dk, dw = qd.cuda(), kd.cuda().expand(B, T_kv, D), w.cuda()
+    dq, dk, dw = qd.cuda(), kd.cuda(), w.cuda()
     d = lcsi.indexer_desc(dq, dk, dw, k, q_pos0)
-    assert d.k_sb == 0
     idx, idx_u, cnt = run_both(d, B, T_q, k)
     assert np.array_equal(idx, idx_u)
     low = cnt < k
     log(f"  rows with fewer than k candidates: {int(low.sum())} of {low.size}")
-    assert low.mean() > 0.9
-    rows = np.array([0, 5])
-    _, r_idx = oracle.score_select(bits(qd[0, rows]), w[0, rows].numpy(), bits(kd[0]), q_pos0 + rows, k,
-                                   want_scores=False)
-    assert np.array_equal(idx[0, rows], r_idx)
+    assert low[:n_hot].all() and not low[n_hot:].any()
+    assert (n_hot * T_q <= RMAX) == (n_hot == 4)
+    for b in (0, n_hot - 1, n_hot):
+        rows = np.array([0, 5])
+        _, r_idx = oracle.score_select(bits(qd[b, rows]), w[b, rows].numpy(), bits(kd[b]), q_pos0 + rows, k,
+                                       want_scores=False)
+        assert np.array_equal(idx[b, rows], r_idx), b
 
 
 def test_fused_long_rows_stream_candidates():
-    """16 heads: 512 sampled scores per row; rows of ~300K keys then keep
-    about 9K candidates, more than the LDS lists hold (8192), so the
-    selection streams them from memory (some rows overflow and are
-    rescored)."""
+    """16 heads: at most 1024 sampled scores per row; rows of ~600K keys
+    then keep about 8K candidates, often more than the LDS lists hold
+    (8192), so the selection streams them from memory (a few rows overflow
+    their slots and are rescored from the list)."""
     B, H, D, k = 256, 16, 64, 2048
-    T_q, q_pos0 = 32, 300000
+    T_q, q_pos0 = 32, 600000
     T_kv = q_pos0 + T_q
     g = torch.Generator().manual_seed(13)
     q = torch.randn((B, T_q, H, D), generator=g).to(torch.bfloat16)
