@@ -227,13 +227,17 @@ def main():
     n_f = sum(pattern)
     score_s = float(np.mean(score_ms)) / 1e3
     kdt = "fp8xfp8" if wl.q_fp8 else ("fp8" if wl.key_fp8 else "bf16")
+    # the fused candidate pass (prefill kernel, 16+ heads): the library plans
+    # it when its workspace needs the candidate slots
+    d_last = plans[-1][3][0]
+    fused = lcsi.idx_score_topk_ws_bytes(d_last) > lcsi.idx_score_topk_ws_bytes(d_last, lcsi.LCSI_UNFUSED)
     peak = PEAK_FP8_TFLOPS if wl.q_fp8 else PEAK_BF16_TFLOPS
     if wl.T_q > 1:
         achieved = pairs * flops_per_pair * n_f / score_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": score_traffic(wl),
-                    "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
+                    "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}{',fused' if fused else ''}>"}
     else:
         # keys (+ fp8 scale) read once per sequence, queries and weights, score row written
         key_b = wl.D_I * (1 if wl.key_fp8 else 2) + (4 if wl.key_fp8 else 0)
@@ -247,8 +251,10 @@ def main():
     roofline["launches_per_step"] = nchunk * n_f
     roofline["avg_launch_ms"] = round(float(np.mean(score_ms)) / (nchunk * n_f), 4)
     # select: HBM-bound; algorithmic bytes = read each causal score once + write k indices
+    # (after the fused pass the selection reads candidates, not score rows:
+    # no figure then)
     sel_bytes = (pairs * 4 + n_q_total * wl.top_k * 4) * n_f
-    sel_gbs = sel_bytes / (float(np.mean(select_ms)) / 1e3) / 1e9
+    sel_gbs = None if fused else round(sel_bytes / (float(np.mean(select_ms)) / 1e3) / 1e9, 1)
     # attention: bytes of the gathered KV rows (576 x bf16 per selected index) + Q + O
     sel_per_row = sum(min(wl.top_k, p + 1) for p in range(wl.q_pos0, wl.q_pos0 + wl.n_q)) * wl.B
     attn_bytes = (sel_per_row * wl.D_qk * 2 + n_q_total * wl.H_q * (wl.D_qk + wl.D_v) * 2) * L
@@ -307,7 +313,8 @@ def main():
         "ms": {"score": round(float(np.mean(score_ms)), 3), "select": round(float(np.mean(select_ms)), 3),
                "attention": round(float(np.mean(attn_ms)), 3), "indexer": round(idx_mean, 3),
                "step_events": round(float(np.mean(step_ms)), 3)},
-        "select_algorithmic_GBps": round(sel_gbs, 1),
+        "select_algorithmic_GBps": sel_gbs,
+        "select_input": "fused candidates" if fused else "score rows",
         "attention_algorithmic_GBps": round(attn_gbs, 1),
         **extra,
     }
