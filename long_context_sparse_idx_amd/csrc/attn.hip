@@ -19,7 +19,10 @@
 //   S^T     : 16x16x32 bf16 MFMA with K as the A operand (16 keys) and Q^T
 //             as B (16 heads), so a lane ends up holding 8 keys of ONE head.
 //             The A-row -> key map is chosen so those 8 keys are consecutive
-//             (8g .. 8g+7 for lane group g).
+//             (8g .. 8g+7 for lane group g).  The two waves of a head group
+//             that own neighbouring output-dim slices each compute one
+//             16-key half and swap halves through LDS, so K is read from LDS
+//             and multiplied once per pair, not once per wave.
 //   softmax : online, in fp32 registers, exp2 with the scale folded in.
 //   PV      : O^T = V^T P^T: the A operand (8 consecutive keys of one V
 //             column) comes from the row-major tile through LDS transpose
@@ -84,6 +87,7 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     constexpr int NW = NWH * NDS;                     // waves per workgroup
     constexpr int DVW = DV / NDS;                     // output dims per wave
     constexpr int NDT = DVW / 16;
+    static_assert(NDS % 2 == 0, "the dim-slice waves of a head group work in pairs");
 
     // Two separately declared buffers, each named at compile time in the
     // unrolled tile loop below: the compiler can then tell that the reads of
@@ -92,6 +96,9 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     // number it waits for every outstanding direct load before each LDS read).
     __shared__ __attribute__((aligned(1024))) uint8_t kv0[BUFB];
     __shared__ __attribute__((aligned(1024))) uint8_t kv1[BUFB];
+    // S^T halves handed between the two waves of a pair (same head group,
+    // neighbouring dim slices): each computes 16 of the tile's 32 keys
+    __shared__ f32x4 sx[NW * 64];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
@@ -159,17 +166,30 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
         const uint32_t vcur = (vmask >> (8 * g)) & 0xFFu;  // this lane's keys 8g .. 8g+7
         const bool any = vmask != 0;
         if (any) {
-            // ---- S^T = K Q^T for 32 keys (two 16-key halves)
-            // (the two halves are independent MFMA chains, interleaved)
-            f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-            const uint8_t *kp = tb + (8 * (l16 >> 2) + (l16 & 3)) * ROWB + 16 * g;
+            // ---- S^T = K Q^T for 32 keys in two 16-key halves: this wave
+            // computes half (ds & 1) -- as two interleaved MFMA chains over
+            // the even and odd k-steps -- and takes the other from its
+            // partner wave through LDS (the waves of a pair hold the same
+            // heads, so lane l of both holds the same (head, keys) slots)
+            const int hf = ds & 1;
+            const uint8_t *kp = tb + (8 * (l16 >> 2) + (l16 & 3) + 4 * hf) * ROWB + 16 * g;
+            f32x4 c0 = f32x4{0, 0, 0, 0}, c1 = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int s = 0; s < QSTEPS; ++s) {
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-                    sacc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 4 * hf * ROWB + 64 * s)), qf[s], sacc[hf], 0, 0, 0);
+            for (int s = 0; s < QSTEPS; s += 2) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 64 * s)),
+                                                             qf[s], c0, 0, 0, 0);
+                if (s + 1 < QSTEPS)
+                    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 64 * (s + 1))), qf[s + 1], c1, 0, 0, 0);
             }
+            const f32x4 own = c0 + c1;
+            sx[wave * 64 + lane] = own;
+            wait_lgkmcnt0();  // (the next tile's direct loads stay in flight)
+            lds_barrier();
+            const f32x4 other = sx[(wave ^ NWH) * 64 + lane];
+            f32x4 sacc[2];
+            sacc[0] = hf ? other : own;
+            sacc[1] = hf ? own : other;
             // ---- online softmax over this lane's keys 8g .. 8g+7 (head l16)
             float sv[8];
             float mt = -__builtin_inff();

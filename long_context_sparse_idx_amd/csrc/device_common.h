@@ -189,6 +189,13 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
+// s_waitcnt on the LDS/scalar-memory counter only: this wave's LDS writes
+// have completed (vector-memory loads still in flight are not waited on).
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 // s_waitcnt on the vector-memory counter only: wait until at most N vector
 // memory operations of this wave are outstanding (N < 64); LDS and export
 // counters are not waited on.
