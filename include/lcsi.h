@@ -124,10 +124,10 @@ typedef struct lcsi_indexer {
  * All query heads attend through the one shared KV head.  Query row t sits
  * at position p_t = q_pos0 + t; an index that is negative, larger than p_t
  * or >= T_kv is skipped (it contributes nothing).  A row with no usable
- * index yields zeros.  Logits are sm_scale * q.k (sm_scale finite).
+ * index yields zeros.  Logits are sm_scale * q.k (sm_scale finite and > 0).
  * Alignment: all base pointers and strides multiples of 16 bytes.
  * Envelope: (D_qk, D_v) in {(128,128), (576,512)}; 1 <= H_q <= 64;
- * 1 <= top_k <= 2048. */
+ * 1 <= top_k <= 2048; k and v row strides below 4 GiB. */
 typedef struct lcsi_attn {
     int32_t B, T_q, T_kv, H_q, D_qk, D_v, top_k;
     float sm_scale;

@@ -28,9 +28,9 @@ CFLAGS = [
 ]
 
 
-# Per-source flags.  score.hip: NaN inputs are outside the indexer's
-# contract, so fmaxf(x, 0) needs no NaN-quieting instruction.
-SOURCE_FLAGS = {"score.hip": ["-fno-honor-nans"]}
+# Per-source flags.  score.hip, attn.hip: NaN inputs are outside the
+# contract, so fmaxf needs no NaN-quieting instruction.
+SOURCE_FLAGS = {"score.hip": ["-fno-honor-nans"], "attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, extra=()) -> str:

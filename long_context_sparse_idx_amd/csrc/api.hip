@@ -66,11 +66,13 @@ int check_attn(const lcsi_attn *a)
     int rc = check_rows(a->B, a->T_q, a->T_kv, a->q_pos0, a->top_k);
     if (rc) return rc;
     if (!a->q || !a->k || !a->v || !a->out) return LCSI_EINVAL;
-    if (a->H_q < 1 || a->D_qk < 1 || a->D_v < 1 || !isfinite(a->sm_scale)) return LCSI_EINVAL;
+    if (a->H_q < 1 || a->D_qk < 1 || a->D_v < 1 || !isfinite(a->sm_scale) || !(a->sm_scale > 0.f)) return LCSI_EINVAL;
     if (a->q_sb < 0 || a->q_st < 0 || a->q_sh < 0 || a->k_sb < 0 || a->k_st < 0 || a->v_sb < 0 || a->v_st < 0 ||
         a->o_sb < 0 || a->o_st < 0 || a->o_sh < 0)
         return LCSI_EINVAL;
     if (a->H_q > 64) return LCSI_EUNSUPPORTED;
+    // KV rows are addressed with 32-bit byte strides
+    if (a->k_st * 2 >= ((int64_t)1 << 32) || a->v_st * 2 >= ((int64_t)1 << 32)) return LCSI_EUNSUPPORTED;
     if (!((a->D_qk == 128 && a->D_v == 128) || (a->D_qk == 576 && a->D_v == 512))) return LCSI_EUNSUPPORTED;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16)) return LCSI_EALIGN;
     if (!mult(a->q_sb, 8) || !mult(a->q_st, 8) || !mult(a->q_sh, 8) || !mult(a->k_sb, 8) || !mult(a->k_st, 8) ||

@@ -71,6 +71,20 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint8_t *p)
 #endif
 }
 
+// max(x[l], x[l ^ 16], x[l ^ 32], x[l ^ 48]) in every lane, with the gfx950
+// row-swap VALU ops (no LDS): with both operands x, v_permlane16_swap
+// returns x of rows (0,0,2,2) and (1,1,3,3) -- their max is the max over
+// the row pair -- and v_permlane32_swap likewise across the two halves.
+__device__ __forceinline__ float max_lane_rows(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const uint32_t v = __float_as_uint(m);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 template <int DQK, int DV, int NWH, int NDS, bool SHARED>
 __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnArgs a)
 {
@@ -97,13 +111,21 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     __shared__ __attribute__((aligned(1024))) uint8_t kv0[BUFB];
     __shared__ __attribute__((aligned(1024))) uint8_t kv1[BUFB];
     // S^T halves handed between the two waves of a pair (same head group,
-    // neighbouring dim slices): each computes 16 of the tile's 32 keys
-    __shared__ f32x4 sx[NW * 64];
+    // neighbouring dim slices): each computes 16 of the tile's 32 keys.  One
+    // array per half, each named at compile time where it is read, so the
+    // compiler can tell these reads from the direct loads still filling the
+    // next tile (through one array it waited for all of them first).
+    __shared__ f32x4 sxa[NW / 2 * 64];
+    __shared__ f32x4 sxb[NW / 2 * 64];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    // (the wave index as a scalar: the LDS destinations of the direct loads
+    // built from it are then scalar too)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4,
+              l16 = lane & 15;
     const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
     const int64_t p = a.q_pos0 + t;
     const int hg = wave % NWH, ds = wave / NWH;
+    const int hf = ds & 1, pr = hg + NWH * (ds >> 1);  // half of S^T this wave computes; its pair
     const int head = hg * 16 + l16;
     const bool head_ok = head < a.H;
     const int j_lo = split * a.split_len;
@@ -139,15 +161,38 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     // chunk c of tile row r).  Unusable indices read row 0 instead (finite
     // data; their keys are masked), pad slots and slots past the tile
     // re-read the row's first chunk.
-    auto gather = [&](int32_t keys, uint8_t *dst) {
+    // The slot -> (tile row, source, byte offset) map of this lane's loads is
+    // the same for every tile: worked out once here.
+    constexpr int MPW = (NDMA + NW - 1) / NW;  // direct loads per wave and tile
+    int g_row[MPW];
+    uint32_t g_off[MPW];
+    bool g_v[MPW];
 #pragma unroll
-        for (int m = wave; m < NDMA; m += NW) {
-            const int slot = 64 * m + lane;
-            const int row = slot / RS, c = slot - row * RS;
-            const int32_t key = __shfl(keys, row < TK ? row : 0);
-            const int64_t kr = (row < TK && key >= 0) ? key : 0;
-            const uint16_t *src = c < NCK ? kbase + kr * a.k_st + 8 * c
-                                 : (c < NCK + NCV ? vbase + kr * a.v_st + 8 * (c - NCK) : kbase + kr * a.k_st);
+    for (int i = 0; i < MPW; ++i) {
+        const int slot = 64 * (wave + NW * i) + lane;
+        const int row = slot / RS, c = slot - row * RS;
+        g_row[i] = row < TK ? row : 0;
+        g_v[i] = c >= NCK && c < NCK + NCV;
+        g_off[i] = c < NCK ? 16 * c : (g_v[i] ? 16 * (c - NCK) : 0);
+    }
+    const uint8_t *kb8 = reinterpret_cast<const uint8_t *>(kbase);
+    const uint8_t *vb8 = reinterpret_cast<const uint8_t *>(vbase);
+    // row strides in bytes (below 4 GiB, checked on the host)
+    const uint32_t kst_b = (uint32_t)(a.k_st * 2), vst_b = (uint32_t)(a.v_st * 2);
+    auto gather = [&](int32_t keys, uint8_t *dst) {
+        // every lane's key of every load first (the shuffles go out back to
+        // back), then the loads
+        uint32_t kr[MPW];
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int32_t key = __shfl(keys, g_row[i]);
+            kr[i] = key >= 0 ? (uint32_t)key : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int m = wave + NW * i;
+            if (m >= NDMA) break;
+            const uint8_t *src = (NCV && g_v[i] ? vb8 + (uint64_t)kr[i] * vst_b : kb8 + (uint64_t)kr[i] * kst_b) + g_off[i];
             load_to_lds16(src, dst + 1024 * m);
         }
     };
@@ -167,11 +212,13 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
         const bool any = vmask != 0;
         if (any) {
             // ---- S^T = K Q^T for 32 keys in two 16-key halves: this wave
-            // computes half (ds & 1) -- as two interleaved MFMA chains over
-            // the even and odd k-steps -- and takes the other from its
-            // partner wave through LDS (the waves of a pair hold the same
-            // heads, so lane l of both holds the same (head, keys) slots)
-            const int hf = ds & 1;
+            // computes half hf -- as two interleaved MFMA chains over the even
+            // and odd k-steps -- and takes the other from its partner wave
+            // through LDS (the waves of a pair hold the same heads, so lane l
+            // of both holds the same (head, key) slots).  Lane (g, head) then
+            // holds keys 8g + 4hf + r (own, r < 4) and 8g + 4(1 - hf) + r
+            // (other); this wave keeps them in that order as its 8 softmax
+            // values and PV k-slots, and reads V's rows in the same order.
             const uint8_t *kp = tb + (8 * (l16 >> 2) + (l16 & 3) + 4 * hf) * ROWB + 16 * g;
             f32x4 c0 = f32x4{0, 0, 0, 0}, c1 = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -183,50 +230,64 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
                         as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 64 * (s + 1))), qf[s + 1], c1, 0, 0, 0);
             }
             const f32x4 own = c0 + c1;
-            sx[wave * 64 + lane] = own;
+            if (hf)
+                sxb[pr * 64 + lane] = own;
+            else
+                sxa[pr * 64 + lane] = own;
             wait_lgkmcnt0();  // (the next tile's direct loads stay in flight)
             lds_barrier();
-            const f32x4 other = sx[(wave ^ NWH) * 64 + lane];
-            f32x4 sacc[2];
-            sacc[0] = hf ? other : own;
-            sacc[1] = hf ? own : other;
-            // ---- online softmax over this lane's keys 8g .. 8g+7 (head l16)
-            float sv[8];
-            float mt = -__builtin_inff();
+            const f32x4 other = hf ? sxa[pr * 64 + lane] : sxb[pr * 64 + lane];
+            // ---- online softmax over this lane's 8 keys (head l16), in
+            // log2 units: logit = sm_scale_log2 * s (sm_scale_log2 > 0, so the
+            // maximum of the raw scores gives the maximum logit)
+            float sr[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sr[r] = own[r];
+                sr[4 + r] = other[r];
+            }
+            if (__builtin_expect(vmask != 0xFFFFFFFFu, 0)) {  // (tile-uniform: only tiles with unusable entries)
+                const uint32_t vk = ((vcur >> (4 * hf)) & 0xFu) | (((vcur >> (4 - 4 * hf)) & 0xFu) << 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (!((vk >> e) & 1u)) sr[e] = -__builtin_inff();
+            }
+            float mt = fmaxf(fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3])), fmaxf(fmaxf(sr[4], sr[5]), fmaxf(sr[6], sr[7])));
+            mt = max_lane_rows(mt) * a.sm_scale_log2;  // over the 4 lane groups: the head's 32 keys
+            // The reference m_run of the exponentials moves only when the
+            // tile's maximum exceeds it by more than 8 (log2 units): the
+            // p values then stay below 2^8 (exact range for bf16 and fp32),
+            // and O and l are rescaled only on such a move, not on every
+            // new maximum (O / l is the same for any reference).
+            const bool bump = mt > m_run + 8.f;  // (from -inf: any usable key)
+            const float m_new = bump ? mt : m_run;
+            // (while no key of the head was usable, every logit is -inf and
+            // p = 2^-inf = 0 against any finite reference)
+            const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            float pv[8];
+            float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const bool ok = (vcur >> e) & 1u;
-                sv[e] = ok ? sacc[e >> 2][e & 3] * a.sm_scale_log2 : -__builtin_inff();
-                mt = fmaxf(mt, sv[e]);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt);
-            float pv[8];
-            float alpha = 1.f, psum = 0.f;
-            if (m_new == -__builtin_inff()) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-            } else {
-                alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
-                    psum += pv[e];
-                }
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[e], a.sm_scale_log2, -m_use));
+                psum += pv[e];
             }
             m_run = m_new;
             l_run = l_run * alpha + psum;
+            if (__ballot(bump)) {
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+                for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+            }
             const bf16x8 pfv = as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                                pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
-            // ---- O^T += V^T P^T; A = column (ds*DVW + dt*16 + l16) of rows 8g .. 8g+7
-            const uint8_t *vp = tb + (8 * g + (l16 >> 2)) * ROWB + VOFF + 2 * (ds * DVW + 4 * (l16 & 3));
+            // ---- O^T += V^T P^T; A = column (ds*DVW + dt*16 + l16) of this
+            // wave's 8 keys in its order: rows 8g + 4hf .. +3, then the other 4
+            const uint8_t *vp = tb + (8 * g + 4 * hf + (l16 >> 2)) * ROWB + VOFF + 2 * (ds * DVW + 4 * (l16 & 3));
+            const int vo = hf ? -4 * ROWB : 4 * ROWB;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const uint2 lo = lds_read_tr(vp + 32 * dt);
-                const uint2 hi = lds_read_tr(vp + 4 * ROWB + 32 * dt);
+                const uint2 hi = lds_read_tr(vp + vo + 32 * dt);
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), pfv,
                                                                    oacc[dt], 0, 0, 0);
             }

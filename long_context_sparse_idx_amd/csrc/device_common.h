@@ -36,12 +36,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return u >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 (the same rounding as f32_to_bf16_bits for finite
+// inputs).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Four OCP E4M3 bytes (one dword) -> four bf16 values packed in two dwords
 // (byte i -> half i), with the hardware conversion at scale 1.  Every finite

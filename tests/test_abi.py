@@ -235,6 +235,8 @@ def test_attn_query_mode():
     ("D_v", 128, lcsi.LCSI_EUNSUPPORTED),
     ("sm_scale", float("inf"), lcsi.LCSI_EINVAL),
     ("sm_scale", float("nan"), lcsi.LCSI_EINVAL),
+    ("sm_scale", 0.0, lcsi.LCSI_EINVAL),
+    ("sm_scale", -0.04, lcsi.LCSI_EINVAL),
     ("q", 0, lcsi.LCSI_EINVAL),
     ("out", 0, lcsi.LCSI_EINVAL),
     ("v", FAKE + 2, lcsi.LCSI_EALIGN),
