@@ -242,6 +242,8 @@ def test_attn_query_mode():
     ("v", FAKE + 2, lcsi.LCSI_EALIGN),
     ("k_st", 580, lcsi.LCSI_EALIGN),
     ("o_sh", 516, lcsi.LCSI_EALIGN),
+    ("k_st", 1 << 31, lcsi.LCSI_EUNSUPPORTED),   # KV row stride of 4 GiB (bf16 elements)
+    ("v_st", 1 << 31, lcsi.LCSI_EUNSUPPORTED),
 ])
 def test_attn_rejects_bad_fields(field, value, code):
     assert call_attn(good_attn(**{field: value}))[0] == code

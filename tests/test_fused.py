@@ -206,3 +206,26 @@ def test_fused_long_rows_stream_candidates():
     log(f"  counts {cnt.min()}..{cnt.max()}, streamed rows {int(streamed.sum())}, "
         f"overflow {int((cnt > CAP).sum())}, below k {int((cnt < k).sum())}")
     assert streamed.sum() > 100
+
+
+@pytest.mark.parametrize("k", [1, 64, 700])
+def test_fused_small_top_k(k):
+    """Sampled rows with a small top-k (the sampled rank r falls to a few
+    samples): the candidates still settle the rows and match the unfused
+    path; integer-exact rows match the oracle."""
+    B, H, D = 1, 64, 128
+    T_q, q_pos0 = 2048, 20000
+    T_kv = q_pos0 + T_q
+    q, kk, w = int_inputs(B, T_q, T_kv, H, D, 100 + k)
+    qd, kd = q.to(torch.bfloat16), kk.to(torch.bfloat16)
+    dq, dk, dw = qd.cuda(), kd.cuda(), w.cuda()
+    d = lcsi.indexer_desc(dq, dk, dw, k, q_pos0)
+    idx, idx_u, cnt = run_both(d, B, T_q, k)
+    assert np.array_equal(idx, idx_u)
+    ok = (cnt >= k) & (cnt <= CAP)
+    log(f"  k={k}: counts {cnt.min()}..{cnt.max()}, unsettled {int((~ok).sum())}")
+    assert ok.mean() > 0.99
+    rows = np.array([0, 1000, 2047])
+    _, r_idx = oracle.score_select(bits(qd[0, rows]), w[0, rows].numpy(), bits(kd[0]), q_pos0 + rows, k,
+                                   want_scores=False)
+    assert np.array_equal(idx[0, rows], r_idx)
