@@ -380,7 +380,7 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
 #define ATTN_SPLIT_TARGET 256   // workgroups aimed at when few rows are present
 #endif
 #ifndef ATTN_MIN_TILES
-#define ATTN_MIN_TILES 2        // index tiles per split at least
+#define ATTN_MIN_TILES 4        // index tiles per split at least (fewer: the fp32 partials outweigh the gather)
 #endif
 
 void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len)
