@@ -570,16 +570,20 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelectArgs a)
         for (int j = tid; j < m; j += NT) out[j] = j;
         return;
     }
-    if (tid == 0) {
-        int acc = 0;
-        bool bad = false;
-        for (int s = 0; s < a.nseg; ++s) {
-            const int c = a.cnt[r * a.nseg + s];
-            bad |= c < 0;
-            pre[s] = acc;
-            acc += c < 0 ? 0 : c;
+    if (tid < 64) {
+        // segment counts (nseg <= 64) -> exclusive prefix by one wave; a
+        // negative count (overflowed segment) marks the row bad (-1 total)
+        const int c = tid < a.nseg ? a.cnt[r * a.nseg + tid] : 0;
+        const int v = c < 0 ? 0 : c;
+        int inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(inc, o);
+            if (tid >= o) inc += u;
         }
-        pre[a.nseg] = bad ? -1 : acc;
+        if (tid < a.nseg) pre[tid] = inc - v;
+        const bool bad = ballot(c < 0) != 0;
+        if (tid == a.nseg - 1) pre[a.nseg] = bad ? -1 : inc;
     }
     __syncthreads();
     const int total = pre[a.nseg];
