@@ -592,8 +592,11 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelectArgs a)
         // wave list, so the lists visited wave by wave stay ascending
         const int per = (total + NW - 1) / NW;
         for (int i = tid; i < total; i += NT) {
+            // segment holding entry i: the last s with pre[s] <= i (binary
+            // search over the ascending prefix; pre[0] = 0)
             int s = 0;
-            while (pre[s + 1] <= i) ++s;  // segment holding entry i
+            for (int step = 32; step >= 1; step >>= 1)
+                if (s + step < a.nseg && pre[s + step] <= i) s += step;
             const int64_t src = (r * a.nseg + s) * SEG_CAP + (i - pre[s]);
             const int v = i / per, j = i - v * per;
             sh.u.cand.key[v * CAPW + j] = a.ckey[src];
