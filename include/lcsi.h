@@ -163,8 +163,8 @@ int64_t lcsi_score_ld(int32_t T_kv);
  * (workspace rule above; it is always required).
  *
  * Fused pass (the default for H_I >= 16 when the prefill kernel runs, i.e.
- * the rows fill the chip or have fewer than 4096 keys, and some row has
- * more than top_k keys): score rows are not written.  The scoring kernel
+ * the rows fill the chip, and the longest row has more than 16384 keys):
+ * score rows are not written.  The scoring kernel
  * keeps, per row, only the scores at or above a threshold drawn from a
  * sample of the row's scores (at most 16384 (score, position) pairs per
  * row) and the selection runs on those; a row whose sample misjudged it

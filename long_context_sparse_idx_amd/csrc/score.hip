@@ -825,7 +825,9 @@ bool score_use_split(const ScoreArgs &a)
 
 bool score_can_fuse(const ScoreArgs &a)
 {
-    return a.H >= 16 && !score_use_split(a) && a.q_pos0 + a.T_q > a.top_k;
+    // only when some row is longer than its candidate slots: shorter rows
+    // would keep every score, as 8-byte pairs against 4-byte score rows
+    return a.H >= 16 && !score_use_split(a) && a.q_pos0 + a.T_q > FUSE_CAP;
 }
 
 int score_key_range(int64_t ks, int64_t k_st_bytes)

@@ -80,20 +80,26 @@ def call_idx(d, idx=FAKE, ws=None, nbytes=None, flags=0, sb=16 * 8, st=8):
 
 def test_indexer_query_mode_returns_workspace_size():
     rows_bytes = 2 * 16 * lcsi.score_ld(100) * 4
-    # default: the fused pass (H_I >= 16, prefill kernel, rows longer than
-    # top_k) adds 256-aligned counts, the 256-aligned list of unsettled rows
-    # (a count and 64 row ids) and 16384 candidate pairs per row
+    # short rows (at most 16384 keys): score rows only
     rc, n = call_idx(good_indexer())
+    assert rc == 0 and n == rows_bytes
+    # the fused pass (H_I >= 16, prefill kernel, a row longer than 16384
+    # keys) adds 256-aligned counts, the 256-aligned list of unsettled rows
+    # (a count and 64 row ids) and 16384 candidate pairs per row
+    # (1024 queries: enough workgroups for the prefill kernel)
+    long_rows = dict(T_q=1024, T_kv=20000, q_pos0=18976, q_sb=1024 * 64 * 128, k_sb=20000 * 128,
+                     w_sb=1024 * 64)
+    long_bytes = 2 * 1024 * lcsi.score_ld(20000) * 4
+    rc, n = call_idx(good_indexer(**long_rows), sb=1024 * 8)
     assert rc == 0
-    assert n == rows_bytes + 256 + 512 + 2 * 16 * 16384 * 8
+    assert n == long_bytes + 2 * 1024 * 4 + 512 + 2 * 1024 * 16384 * 8
     for flags in (lcsi.LCSI_UNFUSED, lcsi.LCSI_SCORES_ONLY, lcsi.LCSI_SCORES_PRESET):
-        rc, n = call_idx(good_indexer(), flags=flags)
-        assert rc == 0 and n == rows_bytes, flags
-    # no fused pass below 16 heads, nor when no row is longer than top_k
-    rc, n = call_idx(good_indexer(H_I=8, q_sh=128, w_sb=16 * 8, w_st=8))
-    assert rc == 0 and n == rows_bytes
-    rc, n = call_idx(good_indexer(top_k=100))
-    assert rc == 0 and n == rows_bytes
+        rc, n = call_idx(good_indexer(**long_rows), sb=1024 * 8, flags=flags)
+        assert rc == 0 and n == long_bytes, flags
+    # no fused pass below 16 heads
+    h8 = dict(long_rows, H_I=8, q_sb=1024 * 8 * 128, q_st=8 * 128, w_sb=1024 * 8, w_st=8)
+    rc, n = call_idx(good_indexer(**h8), sb=1024 * 8)
+    assert rc == 0 and n == long_bytes
     rc, n = call_idx(good_indexer(key_dtype=lcsi.LCSI_KEY_FP8_E4M3, k_scale=FAKE, ks_sb=100,
                                   k_sb=100 * 128, k_st=128))
     assert rc == 0 and n > 0
