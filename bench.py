@@ -227,10 +227,13 @@ def main():
     n_f = sum(pattern)
     score_s = float(np.mean(score_ms)) / 1e3
     kdt = "fp8xfp8" if wl.q_fp8 else ("fp8" if wl.key_fp8 else "bf16")
-    # the fused candidate pass (prefill kernel, 16+ heads): the library plans
-    # it when its workspace needs the candidate slots
-    d_last = plans[-1][3][0]
-    fused = lcsi.idx_score_topk_ws_bytes(d_last) > lcsi.idx_score_topk_ws_bytes(d_last, lcsi.LCSI_UNFUSED)
+    # the fused candidate pass (prefill kernel, 16+ heads, a row longer than
+    # its candidate slots): the library plans it when its workspace needs
+    # the slots; chunks of shorter rows run unfused
+    def plan_fused(d):
+        return lcsi.idx_score_topk_ws_bytes(d) > lcsi.idx_score_topk_ws_bytes(d, lcsi.LCSI_UNFUSED)
+    n_fused = sum(plan_fused(p[3][0]) for p in plans)
+    fused = n_fused > 0
     peak = PEAK_FP8_TFLOPS if wl.q_fp8 else PEAK_BF16_TFLOPS
     if wl.T_q > 1:
         achieved = pairs * flops_per_pair * n_f / score_s / 1e12
@@ -249,6 +252,8 @@ def main():
                     "traffic": score_traffic(wl),
                     "kernel": f"score_splitkey_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
     roofline["launches_per_step"] = nchunk * n_f
+    if fused:
+        roofline["fused_launches_per_step"] = n_fused * n_f
     roofline["avg_launch_ms"] = round(float(np.mean(score_ms)) / (nchunk * n_f), 4)
     # select: HBM-bound; algorithmic bytes = read each causal score once + write k indices
     # (after the fused pass the selection reads candidates, not score rows:
