@@ -105,6 +105,23 @@ def test_indexer_query_mode_returns_workspace_size():
     assert rc == 0 and n > 0
 
 
+@pytest.mark.parametrize("last_row_keys,fused", [(16384, False), (16385, True)])
+def test_fused_pass_needs_a_row_longer_than_the_slots(last_row_keys, fused):
+    """The fused pass is planned only when the longest row (q_pos0 + T_q
+    causal keys) exceeds the 16384 candidate slots of a row, and with enough
+    rows for the prefill kernel (2 x 1024 queries at 64 heads)."""
+    T_q, T_kv = 1024, last_row_keys
+    d = dict(T_q=T_q, T_kv=T_kv, q_pos0=T_kv - T_q, q_sb=T_q * 64 * 128, k_sb=T_kv * 128, w_sb=T_q * 64)
+    rc, n = call_idx(good_indexer(**d), sb=T_q * 8)
+    rc_u, n_u = call_idx(good_indexer(**d), sb=T_q * 8, flags=lcsi.LCSI_UNFUSED)
+    assert rc == 0 and rc_u == 0
+    assert n_u == 2 * T_q * lcsi.score_ld(T_kv) * 4
+    assert (n > n_u) == fused
+    # fewer rows (the split-key kernel scores them): never fused
+    rc, n = call_idx(good_indexer(**dict(d, B=1)), sb=T_q * 8)
+    assert rc == 0 and n == n_u // 2
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("B", 0, lcsi.LCSI_EINVAL),
     ("T_q", 0, lcsi.LCSI_EINVAL),
