@@ -124,15 +124,41 @@ def _ws(nbytes: int, device) -> Optional[torch.Tensor]:
 
 # ------------------------------------------------------------- descriptors
 
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _inner(t: torch.Tensor, name: str, dims: int, dtypes):
+    """The library takes strides for the outer dimensions only: the last
+    one must be contiguous."""
+    _need(t.dim() == dims, f"{name}: expected {dims} dimensions, got {tuple(t.shape)}")
+    _need(t.dtype in dtypes, f"{name}: dtype {t.dtype} not in {dtypes}")
+    _need(t.shape[-1] <= 1 or t.stride(-1) == 1, f"{name}: the last dimension must be contiguous")
+
+
 def indexer_desc(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, top_k: int, q_pos0: int,
                  k_scale: Optional[torch.Tensor] = None, T_kv: Optional[int] = None,
                  q_scale: Optional[torch.Tensor] = None) -> Indexer:
     """q [B,T_q,H,D] bf16, or fp8 e4m3 bytes (uint8 / float8_e4m3fn) with
     q_scale [B,T_q,H] fp32; k [B,T_kv,D] bf16 or fp8 e4m3 bytes with k_scale
     [B,T_kv] fp32; w [B,T_q,H] fp32."""
+    _inner(q, "q", 4, (torch.bfloat16,) + _FP8)
+    _inner(k, "k", 3, (torch.bfloat16,) + _FP8)
+    _inner(w, "w", 3, (torch.float32,))
     B, T_q, H, D = q.shape
-    fp8 = k.dtype in (torch.uint8, torch.float8_e4m3fn)
-    q8 = q.dtype in (torch.uint8, torch.float8_e4m3fn)
+    fp8 = k.dtype in _FP8
+    q8 = q.dtype in _FP8
+    _need(tuple(k.shape[::2]) == (B, D) and tuple(w.shape) == (B, T_q, H), "q, k, w: shapes do not agree")
+    if fp8:
+        _need(k_scale is not None, "k_scale is required with fp8 keys")
+        _inner(k_scale, "k_scale", 2, (torch.float32,))
+    if q8:
+        _need(q_scale is not None, "q_scale is required with fp8 queries")
+        _inner(q_scale, "q_scale", 3, (torch.float32,))
     d = Indexer()
     d.B, d.T_q, d.H_I, d.D_I, d.top_k = B, T_q, H, D, top_k
     d.T_kv = k.shape[1] if T_kv is None else T_kv
@@ -159,6 +185,8 @@ def attn_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tens
               q_pos0: int, sm_scale: float, T_kv: Optional[int] = None) -> Attn:
     """q [B,T_q,H,Dqk]; k [B,T_kv,Dqk]; v [B,T_kv,Dv] (may be a column view of
     k); out [B,T_q,H,Dv]; all bf16."""
+    for t, name, dims in ((q, "q", 4), (k, "k", 3), (v, "v", 3), (out, "out", 4)):
+        _inner(t, name, dims, (torch.bfloat16,))
     B, T_q, H, Dqk = q.shape
     d = Attn()
     d.B, d.T_q, d.H_q, d.D_qk, d.D_v, d.top_k = B, T_q, H, Dqk, v.shape[-1], top_k
@@ -187,6 +215,7 @@ def idx_score_topk(desc: Indexer, idx: Optional[torch.Tensor], ws: torch.Tensor,
     an index-cache slot), ws: score workspace (see idx_score_topk_ws_bytes)."""
     cap = ctypes.c_size_t(ws.numel() * ws.element_size())
     if idx is not None:
+        _inner(idx, "idx", 3, (torch.int32,))
         sb, st = idx_strides if idx_strides is not None else idx.stride()[:2]
     else:
         sb = st = 0
@@ -203,11 +232,12 @@ def sparse_attn_ws_bytes(desc: Attn) -> int:
 
 def sparse_attn(desc: Attn, idx: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None,
                 idx_strides: Optional[Sequence[int]] = None):
+    _inner(idx, "idx", 3, (torch.int32,))
     sb, st = idx_strides if idx_strides is not None else idx.stride()[:2]
     if ws is None:
         need = sparse_attn_ws_bytes(desc)
         ws = _ws(need, idx.device)
-    cap = ctypes.c_size_t(ws.numel() * 4) if ws is not None else None
+    cap = ctypes.c_size_t(ws.numel() * ws.element_size()) if ws is not None else None
     _check(lib.sparse_attn(ctypes.byref(desc), _ptr(idx), sb, st, _ptr(ws),
                            ctypes.byref(cap) if cap is not None else None, _stream(stream)),
            "sparse_attn")
@@ -226,7 +256,7 @@ def run_layer_group(pattern: Sequence[int], idx_descs: Sequence[Indexer], attn_d
         need = layer_group_ws_bytes(pattern, idx_descs, attn_descs, idx_cache, n_slots, slot_stride,
                                     idx_sb, idx_st)
         ws = _ws(need, idx_cache.device)
-    cap = ctypes.c_size_t(ws.numel() * 4) if ws is not None else None
+    cap = ctypes.c_size_t(ws.numel() * ws.element_size()) if ws is not None else None
     ev = None
     if events is not None:
         # torch creates its events lazily on the first record; create them

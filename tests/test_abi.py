@@ -10,6 +10,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from long_context_sparse_idx_amd import lcsi
 
@@ -314,3 +315,41 @@ def test_layer_group_query_and_pattern_errors():
     assert call_group([1, 0], attn_over={"top_k": 16})[0] == lcsi.LCSI_EINVAL
     assert call_group([1, 0], idx_over={"H_I": 48})[0] == lcsi.LCSI_EUNSUPPORTED
     assert call_group([1, 0], attn_over={"D_qk": 64})[0] == lcsi.LCSI_EUNSUPPORTED
+
+
+def test_binding_checks_layouts_and_dtypes():
+    """The descriptors carry strides for the outer dimensions only: the
+    binding refuses tensors whose last dimension is not contiguous, and wrong
+    dtypes or shapes, before anything reaches the library."""
+    B, T, H, D = 1, 8, 16, 64
+    q = torch.zeros(B, T, H, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, T, D, dtype=torch.bfloat16)
+    w = torch.zeros(B, T, H, dtype=torch.float32)
+    d = lcsi.indexer_desc(q, k, w, 4, 0)
+    assert (d.q_sb, d.q_st, d.q_sh, d.k_st, d.w_st) == (T * H * D, H * D, D, D, H)
+    bad = [
+        dict(q=torch.zeros(B, T, D, H, dtype=torch.bfloat16).transpose(2, 3)),
+        dict(k=torch.zeros(B, D, T, dtype=torch.bfloat16).transpose(1, 2)),
+        dict(w=w.double()),
+        dict(q=q.float()),
+        dict(w=torch.zeros(B, T, H + 1)),
+        dict(k=torch.zeros(B, T, D, dtype=torch.uint8)),  # fp8 keys without k_scale
+    ]
+    for over in bad:
+        args = dict(q=q, k=k, w=w)
+        args.update(over)
+        with pytest.raises(ValueError):
+            lcsi.indexer_desc(args["q"], args["k"], args["w"], 4, 0)
+    with pytest.raises(ValueError):  # fp8 queries without q_scale
+        lcsi.indexer_desc(torch.zeros(B, T, H, D, dtype=torch.uint8), torch.zeros(B, T, D, dtype=torch.uint8),
+                          w, 4, 0, k_scale=torch.ones(B, T))
+    kv = torch.zeros(B, T, 576, dtype=torch.bfloat16)
+    qa = torch.zeros(B, T, 4, 576, dtype=torch.bfloat16)
+    out = torch.zeros(B, T, 4, 512, dtype=torch.bfloat16)
+    a = lcsi.attn_desc(qa, kv, kv[..., :512], out, 4, 0, 0.1)
+    assert (a.k_st, a.v_st, a.o_sh) == (576, 576, 512)
+    with pytest.raises(ValueError):
+        lcsi.attn_desc(qa, kv, kv[..., :512], torch.zeros(B, T, 512, 4, dtype=torch.bfloat16).transpose(2, 3),
+                       4, 0, 0.1)
+    with pytest.raises(ValueError):
+        lcsi.attn_desc(qa.float(), kv, kv[..., :512], out, 4, 0, 0.1)
