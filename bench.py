@@ -161,8 +161,9 @@ def main():
                     help="run one plain 1 GiB device-to-device copy first (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
+              "multi-GPU mode (every step is row-local; a sharded layout is described, not built)",
+              file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.calibrate_copy:
