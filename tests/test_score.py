@@ -34,6 +34,8 @@ def gpu_indexer(q, k, w, top_k, q_pos0, k_scale=None, q_scale=None):
     ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4, dtype=torch.float32, device="cuda")
     idx = torch.empty((B, T_q, top_k), dtype=torch.int32, device="cuda")
     idx_u = torch.empty_like(idx)
+    fused = lcsi.idx_score_topk_ws_bytes(d) > lcsi.idx_score_topk_ws_bytes(d, lcsi.LCSI_UNFUSED)
+    log(f"  fused candidate pass: {fused}")
     lcsi.idx_score_topk(d, idx, ws)
     lcsi.idx_score_topk(d, idx_u, ws, flags=lcsi.LCSI_UNFUSED)
     torch.cuda.synchronize()
@@ -91,6 +93,7 @@ SHAPES = [
     # B, T_q, T_kv, q_pos0, H, D, k         kernel the library picks
     (1, 300, 300, 0, 4, 64, 64),           # prefill (LDS-staged), causal from 0
     (1, 2048, 4100, 2052, 64, 128, 256),   # prefill, offset chunk, ragged key tail
+    (1, 2048, 18000, 15952, 64, 128, 256),  # prefill, rows past 16384 keys: fused candidate pass
     (1, 130, 1000, 870, 16, 128, 100),     # prefill, H=16
     (3, 1, 9001, 9000, 64, 128, 2048),     # decode rows: split-key
     (2, 3, 8192, 8189, 8, 64, 512),        # few rows: split-key, H=8, D=64
