@@ -295,6 +295,22 @@ struct CandSeg {
     }
 };
 
+// Candidates stored contiguously in the LDS candidate arrays (ascending
+// positions), cut into NW consecutive segments of `seg` entries.
+struct LdsPairSeg {
+    const Shared *sh;
+    int n, seg;
+    __device__ int len(int w) const { return seg; }
+    __device__ bool get(int w, int j, uint32_t &key, int32_t &pos) const
+    {
+        const int i = w * seg + j;
+        if (j >= seg || i >= n) return false;
+        key = sh->u.cand.key[i];
+        pos = sh->u.cand.idx[i];
+        return true;
+    }
+};
+
 struct GlobalSeg {
     const float *row;
     int64_t n, seg;
@@ -331,26 +347,44 @@ struct GlobalPairSeg {
 __device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t n, int32_t *out, int k)
 {
     const int tid = threadIdx.x;
+    const int seg = ((c + NW - 1) / NW + 63) / 64 * 64;
     if (c <= NW * CAPW) {
-        // cut into NW consecutive parts, one per wave list, so the lists
-        // visited wave by wave stay ascending
-        const int per = (c + NW - 1) / NW;
-        for (int i = tid; i < c; i += NT) {
-            const u32x2 e = *reinterpret_cast<const u32x2 *>(cp + 2 * i);
-            const int v = i / per, j = i - v * per;
-            sh.u.cand.key[v * CAPW + j] = order_key(__uint_as_float(e.x));
-            sh.u.cand.idx[v * CAPW + j] = (int32_t)e.y;
+        // all loads of a thread issued before the first store (two pairs per
+        // 16-byte range-checked load: pairs past the count read as zeros and
+        // are not stored), the candidates kept contiguous in position order
+        constexpr int IT = NW * CAPW / (2 * NT);
+        u32x4 e[IT];
+#pragma unroll
+        for (int u = 0; u < IT; ++u) e[u] = ld16_ranged(cp, (uint32_t)c * 8u, 16u * (uint32_t)(tid + u * NT));
+#pragma unroll
+        for (int u = 0; u < IT; ++u) {
+            const int i = 2 * (tid + u * NT);
+            if (i < c) {
+                sh.u.cand.key[i] = order_key(__uint_as_float(e[u].x));
+                sh.u.cand.idx[i] = (int32_t)e[u].y;
+            }
+            if (i + 1 < c) {
+                sh.u.cand.key[i + 1] = order_key(__uint_as_float(e[u].z));
+                sh.u.cand.idx[i + 1] = (int32_t)e[u].w;
+            }
         }
-        if (tid < NW) sh.wcnt[tid] = max(0, min(per, c - tid * per));
         __syncthreads();
-        radix_find(sh, Candidates{&sh}, k);
-        emit(sh, CandSeg{&sh}, out, k);
+        radix_find(sh, LdsKeys{sh.u.cand.key, c}, k);
+        emit(sh, LdsPairSeg{&sh, c, seg}, out, k);
         return;
     }
-    const int seg = ((c + NW - 1) / NW + 63) / 64 * 64;
     if (c == n && n <= NLDS) {
         // every score passed: the candidates are the row, positions 0 .. n-1
-        for (int i = tid; i < c; i += NT) sh.u.keys[i] = order_key(__uint_as_float(cp[2 * i]));
+        constexpr int IT = NLDS / (2 * NT);
+        u32x4 e[IT];
+#pragma unroll
+        for (int u = 0; u < IT; ++u) e[u] = ld16_ranged(cp, (uint32_t)c * 8u, 16u * (uint32_t)(tid + u * NT));
+#pragma unroll
+        for (int u = 0; u < IT; ++u) {
+            const int i = 2 * (tid + u * NT);
+            if (i < c) sh.u.keys[i] = order_key(__uint_as_float(e[u].x));
+            if (i + 1 < c) sh.u.keys[i + 1] = order_key(__uint_as_float(e[u].z));
+        }
         __syncthreads();
         radix_find(sh, LdsKeys{sh.u.keys, c}, k);
         emit(sh, LdsSeg{&sh, c, seg}, out, k);
@@ -461,13 +495,19 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     }
 
     if (n <= NLDS) {
-        // ---- path A: whole row in LDS
-        for (int i = 4 * tid; i < n; i += 4 * NT) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + i);
-            sh.u.keys[i] = order_key(v.x);
-            if (i + 1 < n) sh.u.keys[i + 1] = order_key(v.y);
-            if (i + 2 < n) sh.u.keys[i + 2] = order_key(v.z);
-            if (i + 3 < n) sh.u.keys[i + 3] = order_key(v.w);
+        // ---- path A: whole row in LDS (all loads of a thread issued before
+        // the first store; range-checked, so nothing past the row is read)
+        constexpr int IT = NLDS / (4 * NT);
+        u32x4 v[IT];
+#pragma unroll
+        for (int u = 0; u < IT; ++u) v[u] = ld16_ranged(row, (uint32_t)n * 4u, 16u * (uint32_t)(tid + u * NT));
+#pragma unroll
+        for (int u = 0; u < IT; ++u) {
+            const int i = 4 * (tid + u * NT);
+            if (i < n) sh.u.keys[i] = order_key(__uint_as_float(v[u].x));
+            if (i + 1 < n) sh.u.keys[i + 1] = order_key(__uint_as_float(v[u].y));
+            if (i + 2 < n) sh.u.keys[i + 2] = order_key(__uint_as_float(v[u].z));
+            if (i + 3 < n) sh.u.keys[i + 3] = order_key(__uint_as_float(v[u].w));
         }
         __syncthreads();
         radix_find(sh, LdsKeys{sh.u.keys, (int)n}, k);
