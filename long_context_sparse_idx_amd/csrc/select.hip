@@ -65,6 +65,7 @@ struct Shared {
     uint32_t kth;
     int rem;
     int ge;
+    int full;  // the bin holding the rank-th key is taken whole
     uint32_t kmin, kmax;
 };
 
@@ -204,6 +205,7 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 3
                         sh.kth = prefix | ((uint32_t)(4 * lane + e) << shift);
                         sh.rem = rem - acc;
                         sh.ge = (rank - rem) + acc + (int)c[e];  // keys at or above this bin
+                        sh.full = (int)c[e] == rem - acc;
                         break;
                     }
                     acc += (int)c[e];
@@ -215,10 +217,21 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 3
         rem = sh.rem;
         mask |= dmask << shift;
         if (shift == 0 || (msb - shift + 1 >= resolve && sh.ge <= max_ge)) break;
+        if (resolve == 32 && sh.full && prefix != 0) {
+            // every key of the bin is taken: the keys above offset prefix - 1
+            // (this bin and everything above it) are exactly the top `rank`,
+            // so the threshold is prefix - 1 with no ties to count
+            prefix -= 1;
+            rem = 0;
+            break;
+        }
         hi = shift - 1;
     }
     __syncthreads();  // every thread has read sh.kth / sh.rem above
-    if (tid == 0) sh.kth = kmin + prefix;
+    if (tid == 0) {
+        sh.kth = kmin + prefix;
+        sh.rem = rem;
+    }
     __syncthreads();
 }
 
