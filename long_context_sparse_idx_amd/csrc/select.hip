@@ -66,6 +66,7 @@ struct Shared {
     int rem;
     int ge;
     int full;  // the bin holding the rank-th key is taken whole
+    uint32_t wmin[NW], wmax[NW];  // per-wave key range, written while filling LDS
     uint32_t kmin, kmax;
 };
 
@@ -131,31 +132,61 @@ struct GlobalPairs {
 // rank-th key that at least `rank` and at most max_ge keys reach (used for
 // the sampled threshold, where only a bound is needed; max_ge keeps the
 // bound tight when the keys span a wide range, e.g. scores of both signs).
-template <class Src>
-__device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 32, int max_ge = 0x7FFFFFFF)
+// The smallest and largest of a thread's keys (kmn, kmx) reduced over the
+// wave into its slot of sh.wmin / sh.wmax (every wave writes its slot; a
+// wave without keys writes the empty range).  Callers that fill LDS do this
+// before the barrier that ends the fill, so radix_find(..., ranged = true)
+// needs no pass of its own over the keys for their range.
+__device__ __forceinline__ void wave_range(Shared &sh, uint32_t kmn, uint32_t kmx)
 {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0) {
-        sh.kmin = 0xFFFFFFFFu;
-        sh.kmax = 0u;
-    }
-    __syncthreads();
-    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    src.visit([&](uint32_t key) {
-        kmn = min(kmn, key);
-        kmx = max(kmx, key);
-    });
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         kmn = min(kmn, (uint32_t)__shfl_xor(kmn, o));
         kmx = max(kmx, (uint32_t)__shfl_xor(kmx, o));
     }
-    if (lane == 0) {
-        atomicMin(&sh.kmin, kmn);
-        atomicMax(&sh.kmax, kmx);
+    if ((threadIdx.x & 63) == 0) {
+        sh.wmin[threadIdx.x >> 6] = kmn;
+        sh.wmax[threadIdx.x >> 6] = kmx;
     }
-    __syncthreads();
-    const uint32_t kmin = sh.kmin, range = sh.kmax - kmin;
+}
+
+template <class Src>
+__device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 32, int max_ge = 0x7FFFFFFF,
+                           bool ranged = false)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint32_t kmin_all = 0xFFFFFFFFu, kmax_all = 0u;
+    if (ranged) {
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            kmin_all = min(kmin_all, sh.wmin[v]);
+            kmax_all = max(kmax_all, sh.wmax[v]);
+        }
+    } else {
+        if (tid == 0) {
+            sh.kmin = 0xFFFFFFFFu;
+            sh.kmax = 0u;
+        }
+        __syncthreads();
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+        src.visit([&](uint32_t key) {
+            kmn = min(kmn, key);
+            kmx = max(kmx, key);
+        });
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            kmn = min(kmn, (uint32_t)__shfl_xor(kmn, o));
+            kmx = max(kmx, (uint32_t)__shfl_xor(kmx, o));
+        }
+        if (lane == 0) {
+            atomicMin(&sh.kmin, kmn);
+            atomicMax(&sh.kmax, kmx);
+        }
+        __syncthreads();
+        kmin_all = sh.kmin;
+        kmax_all = sh.kmax;
+    }
+    const uint32_t kmin = kmin_all, range = kmax_all - kmin;
     if (range == 0) {  // all keys equal: the rank-th is that key
         if (tid == 0) {
             sh.kth = kmin;
@@ -369,20 +400,28 @@ __device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t
         u32x4 e[IT];
 #pragma unroll
         for (int u = 0; u < IT; ++u) e[u] = ld16_ranged(cp, (uint32_t)c * 8u, 16u * (uint32_t)(tid + u * NT));
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
             const int i = 2 * (tid + u * NT);
             if (i < c) {
-                sh.u.cand.key[i] = order_key(__uint_as_float(e[u].x));
+                const uint32_t key = order_key(__uint_as_float(e[u].x));
+                sh.u.cand.key[i] = key;
                 sh.u.cand.idx[i] = (int32_t)e[u].y;
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
             }
             if (i + 1 < c) {
-                sh.u.cand.key[i + 1] = order_key(__uint_as_float(e[u].z));
+                const uint32_t key = order_key(__uint_as_float(e[u].z));
+                sh.u.cand.key[i + 1] = key;
                 sh.u.cand.idx[i + 1] = (int32_t)e[u].w;
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
             }
         }
+        wave_range(sh, kmn, kmx);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.cand.key, c}, k);
+        radix_find(sh, LdsKeys{sh.u.cand.key, c}, k, 32, 0x7FFFFFFF, true);
         emit(sh, LdsPairSeg{&sh, c, seg}, out, k);
         return;
     }
@@ -392,14 +431,26 @@ __device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t
         u32x4 e[IT];
 #pragma unroll
         for (int u = 0; u < IT; ++u) e[u] = ld16_ranged(cp, (uint32_t)c * 8u, 16u * (uint32_t)(tid + u * NT));
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
             const int i = 2 * (tid + u * NT);
-            if (i < c) sh.u.keys[i] = order_key(__uint_as_float(e[u].x));
-            if (i + 1 < c) sh.u.keys[i + 1] = order_key(__uint_as_float(e[u].z));
+            if (i < c) {
+                const uint32_t key = order_key(__uint_as_float(e[u].x));
+                sh.u.keys[i] = key;
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
+            }
+            if (i + 1 < c) {
+                const uint32_t key = order_key(__uint_as_float(e[u].z));
+                sh.u.keys[i + 1] = key;
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
+            }
         }
+        wave_range(sh, kmn, kmx);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.keys, c}, k);
+        radix_find(sh, LdsKeys{sh.u.keys, c}, k, 32, 0x7FFFFFFF, true);
         emit(sh, LdsSeg{&sh, c, seg}, out, k);
         return;
     }
@@ -514,16 +565,26 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
         u32x4 v[IT];
 #pragma unroll
         for (int u = 0; u < IT; ++u) v[u] = ld16_ranged(row, (uint32_t)n * 4u, 16u * (uint32_t)(tid + u * NT));
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+        auto put = [&](int i, uint32_t bits) {
+            if (i < n) {
+                const uint32_t key = order_key(__uint_as_float(bits));
+                sh.u.keys[i] = key;
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
+            }
+        };
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
             const int i = 4 * (tid + u * NT);
-            if (i < n) sh.u.keys[i] = order_key(__uint_as_float(v[u].x));
-            if (i + 1 < n) sh.u.keys[i + 1] = order_key(__uint_as_float(v[u].y));
-            if (i + 2 < n) sh.u.keys[i + 2] = order_key(__uint_as_float(v[u].z));
-            if (i + 3 < n) sh.u.keys[i + 3] = order_key(__uint_as_float(v[u].w));
+            put(i, v[u].x);
+            put(i + 1, v[u].y);
+            put(i + 2, v[u].z);
+            put(i + 3, v[u].w);
         }
+        wave_range(sh, kmn, kmx);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.keys, (int)n}, k);
+        radix_find(sh, LdsKeys{sh.u.keys, (int)n}, k, 32, 0x7FFFFFFF, true);
         const int seg = (int)(((n + NW - 1) / NW + 63) / 64 * 64);
         emit(sh, LdsSeg{&sh, (int)n, seg}, out, k);
         return;
