@@ -702,24 +702,43 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelectArgs a)
     __syncthreads();
     const int total = pre[a.nseg];
     if (total >= k && total <= NW * CAPW) {
-        // the concatenated lists, cut into NW consecutive parts: one per
-        // wave list, so the lists visited wave by wave stay ascending
-        const int per = (total + NW - 1) / NW;
-        for (int i = tid; i < total; i += NT) {
-            // segment holding entry i: the last s with pre[s] <= i (binary
-            // search over the ascending prefix; pre[0] = 0)
-            int s = 0;
-            for (int step = 32; step >= 1; step >>= 1)
-                if (s + step < a.nseg && pre[s + step] <= i) s += step;
-            const int64_t src = (r * a.nseg + s) * SEG_CAP + (i - pre[s]);
-            const int v = i / per, j = i - v * per;
-            sh.u.cand.key[v * CAPW + j] = a.ckey[src];
-            sh.u.cand.idx[v * CAPW + j] = a.cidx[src];
+        // the concatenated lists, contiguous in LDS (ascending positions);
+        // every load of a thread is issued before the first store
+        constexpr int IT = NW * CAPW / NT;
+        uint32_t kv[IT];
+        int32_t iv[IT];
+#pragma unroll
+        for (int u = 0; u < IT; ++u) {
+            const int i = tid + u * NT;
+            kv[u] = 0u;
+            iv[u] = 0;
+            if (i < total) {
+                // segment holding entry i: the last s with pre[s] <= i
+                // (binary search over the ascending prefix; pre[0] = 0)
+                int s = 0;
+                for (int step = 32; step >= 1; step >>= 1)
+                    if (s + step < a.nseg && pre[s + step] <= i) s += step;
+                const int64_t src = (r * a.nseg + s) * SEG_CAP + (i - pre[s]);
+                kv[u] = a.ckey[src];
+                iv[u] = a.cidx[src];
+            }
         }
-        if (tid < NW) sh.wcnt[tid] = max(0, min(per, total - tid * per));
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+        for (int u = 0; u < IT; ++u) {
+            const int i = tid + u * NT;
+            if (i < total) {
+                sh.u.cand.key[i] = kv[u];
+                sh.u.cand.idx[i] = iv[u];
+                kmn = min(kmn, kv[u]);
+                kmx = max(kmx, kv[u]);
+            }
+        }
+        wave_range(sh, kmn, kmx);
         __syncthreads();
-        radix_find(sh, Candidates{&sh}, k);
-        emit(sh, CandSeg{&sh}, out, k);
+        radix_find(sh, LdsKeys{sh.u.cand.key, total}, k, 32, 0x7FFFFFFF, true);
+        const int seg = ((total + NW - 1) / NW + 63) / 64 * 64;
+        emit(sh, LdsPairSeg{&sh, total, seg}, out, k);
         return;
     }
     // path C: exact, streaming the row from memory
