@@ -171,12 +171,14 @@ def test_score_weight_scaling_and_h1_identity():
     assert np.array_equal(i1, i2)
 
 
+@pytest.mark.parametrize("T_kv", [6000, 20000])
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_prefill_and_splitkey_kernels_agree_bitwise(fmt):
-    """The same rows scored as one batch of many rows (prefill kernel) and as
-    single-row calls (split-key kernel) give identical bits: chunking never
-    changes a score."""
-    T_kv, H, D, k = 6000, 64, 128, 512
+def test_prefill_and_splitkey_kernels_agree_bitwise(fmt, T_kv):
+    """The same rows scored as one batch of many rows (prefill kernel; with
+    20000 keys through the fused candidate pass) and as single-row calls
+    (split-key kernel) give identical bits: chunking never changes a score
+    or an index."""
+    H, D, k = 64, 128, 512
     T_q, q_pos0 = 2048, T_kv - 2048   # 256 workgroups: the prefill kernel
     base = inputs.WORKLOADS[{"bf16": "prefill200k", "k8": "prefill1m", "qk8": "prefill1m_q8"}[fmt]]
     wl = dataclasses.replace(base, name="agree", B=1, T_q=T_q, n_q=T_q, q_pos0=q_pos0, T_kv=T_kv,
