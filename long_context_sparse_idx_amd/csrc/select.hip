@@ -464,14 +464,21 @@ __device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t
 __device__ uint32_t sampled_threshold(Shared &sh, const float *row, int64_t n, int k)
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int s = w * (NSB / NW); s < (w + 1) * (NSB / NW); ++s) {
+    constexpr int RPW = NSB / NW;  // runs per wave, all loads issued first
+    f32x4 v[RPW];
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+        const int s = w * RPW + u;
         const int64_t start = ((n - SBL) * s / (NSB - 1)) & ~(int64_t)3;
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
-        uint32_t *d = sh.u.samp + s * SBL + 4 * lane;
-        d[0] = order_key(v.x);
-        d[1] = order_key(v.y);
-        d[2] = order_key(v.z);
-        d[3] = order_key(v.w);
+        v[u] = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+        uint32_t *d = sh.u.samp + (w * RPW + u) * SBL + 4 * lane;
+        d[0] = order_key(v[u].x);
+        d[1] = order_key(v[u].y);
+        d[2] = order_key(v[u].z);
+        d[3] = order_key(v[u].w);
     }
     __syncthreads();
     int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
