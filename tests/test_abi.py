@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 import torch
@@ -353,3 +354,19 @@ def test_binding_checks_layouts_and_dtypes():
                        4, 0, 0.1)
     with pytest.raises(ValueError):
         lcsi.attn_desc(qa.float(), kv, kv[..., :512], out, 4, 0, 0.1)
+
+
+def test_binding_refuses_to_load_without_the_library(tmp_path):
+    """No fallback: a copy of the binding next to no built library raises
+    ImportError on import instead of running anything else."""
+    pkg = tmp_path / "pkg_no_lib"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text("")
+    src = os.path.join(os.path.dirname(lcsi.__file__), "lcsi.py")
+    (pkg / "lcsi.py").write_text(open(src).read())
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import pkg_no_lib.lcsi\nexcept ImportError as e:\n    print('refused:', e)\n"
+            "else:\n    print('loaded')\n") % str(tmp_path)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("refused:") and "no fallback" in r.stdout, r.stdout
