@@ -37,26 +37,36 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lcsi_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# LCSI_ORACLE_LIB names another build of the same source to load instead
+# (the mutation test points it at deliberately broken copies); it is never
+# rebuilt here.
+_LIB_OVERRIDE = os.environ.get("LCSI_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lib = None
+
+
+GCC_FLAGS = ["-O2", "-fPIC", "-shared", "-std=c11", "-D_GNU_SOURCE", "-Wall"]
+
+
+def compile_source(src: str, out: str) -> None:
+    """gcc the C oracle source `src` into the shared library `out`."""
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", out, src, "-lm", "-lpthread"], check=True)
 
 
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc into oracle/liboracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.run(
-            ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-D_GNU_SOURCE",
-             "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"],
-            check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+    lib = os.path.join(_HERE, "liboracle.so")
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp"
+        compile_source(_SRC, tmp)
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p

@@ -127,6 +127,23 @@ def test_score_select_golden_fixture():
     assert idx[0].tolist() == g["topk3_p1"]
 
 
+def test_score_below_fp32_range_is_stored_as_plus_zero():
+    """A negative score too small for fp32 rounds to zero; the oracle stores
+    +0 (sign bit clear), never -0, so a score row compares bit for bit with
+    one whose -0 results are folded (the reading that -0 counts as +0).
+    Here the only product is 2^-133 * 2^-133 (the smallest bf16 subnormal
+    squared) under a weight of -1: the exact score is -2^-266."""
+    q = np.zeros((1, 1, 8), np.uint16)
+    keys = np.zeros((2, 8), np.uint16)
+    q[0, 0, 0] = 0x0001
+    keys[:, 0] = 0x0001
+    w = np.array([[-1.0]], np.float32)
+    s, idx = oracle.score_select(q, w, keys, [1], 1)
+    assert s[0, 0] == 0.0 and s[0, 1] == 0.0
+    assert not np.signbit(s[0, :2]).any()
+    assert idx[0].tolist() == [0]
+
+
 def _int_inputs(rng, R, H, D, N):
     q = rng.integers(-8, 9, (R, H, D)).astype(np.float32)
     k = rng.integers(-8, 9, (N, D)).astype(np.float32)
