@@ -217,3 +217,26 @@ def test_degenerate_rows(fmt):
             check_scores(S[0, t, :n], rS[t, :n], f"T_kv={T_kv} t={t}")
             assert np.array_equal(idx[0, t], ridx[t]), f"T_kv={T_kv} t={t}: {idx[0, t][:8]} vs {ridx[t][:8]}"
             assert (idx[0, t, min(n, k):] == -1).all()
+
+
+def test_fp8_keys_widen_exactly_for_every_finite_code():
+    """The fp8-key path widens e4m3 keys to bf16 with the hardware conversion
+    at scale 1: exact for every finite code.  Key s holds code s in its first
+    element (the two NaN codes replaced by zero), one head reads it with +1
+    and another row with -1, so the scores are ReLU(+-value) bit for bit."""
+    codes = np.array([c if (c & 0x7F) != 0x7F else 0 for c in range(256)], np.uint8)
+    T_kv, T_q, H, D = 256, 2, 4, 64
+    k = torch.zeros((1, T_kv, D), dtype=torch.uint8)
+    k[0, :, 0] = torch.from_numpy(codes)
+    q = torch.zeros((1, T_q, H, D), dtype=torch.float32)
+    q[0, 0, 0, 0], q[0, 1, 0, 0] = 1.0, -1.0
+    w = torch.zeros((1, T_q, H), dtype=torch.float32)
+    w[0, :, 0] = 1.0
+    ks = torch.ones((1, T_kv), dtype=torch.float32)
+    S, _ = gpu_indexer(q.to(torch.bfloat16).cuda(), k.cuda(), w.cuda(), 8, T_kv - T_q, k_scale=ks.cuda())
+    val = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    n0 = T_kv - 1  # row 0 sees keys 0 .. 254
+    want0 = (np.maximum(val[:n0], 0) + 0.0).astype(np.float32)   # (+0.0 folds a -0)
+    want1 = (np.maximum(-val, 0) + 0.0).astype(np.float32)
+    assert np.array_equal(S[0, 0, :n0].view(np.uint32), want0.view(np.uint32))
+    assert np.array_equal(S[0, 1, :T_kv].view(np.uint32), want1.view(np.uint32))
