@@ -158,8 +158,10 @@ int64_t lcsi_score_ld(int32_t T_kv);
  * B*T_q*ld*4 bytes rounded up to 256, plus, when few long rows are selected
  * (B*T_q <= 128 rows of >= 32768 keys: decode), the selection's candidate
  * lists after the rows, plus, when the call takes the fused pass below,
- * B*T_q*4 bytes (rounded up to 256) of counts and B*T_q*16384*8 bytes of
- * candidate slots; query mode returns the total for the given flags
+ * B*T_q*4 bytes (rounded up to 256) of counts, 512 bytes for the list of
+ * unsettled rows (a count and 64 row ids, rounded up to 256) and
+ * B*T_q*16384*8 bytes of candidate slots; query mode returns the total for
+ * the given flags
  * (workspace rule above; it is always required).
  *
  * Fused pass (the default for H_I >= 16 when the prefill kernel runs, i.e.
@@ -212,7 +214,8 @@ int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
  *              stream); query mode returns the largest single requirement.
  *   events     optional HOST array of 4*L hipEvent_t (as void*), or NULL.
  *              For layer l: [4l] before the layer, [4l+1] after scoring
- *              (with the fused pass: after it and the rescoring launch),
+ *              (with the fused pass: after it and the two rescoring
+ *              launches),
  *              [4l+2] after selection, [4l+3] after attention (for an S
  *              layer the first three are recorded at the same point).
  * Pattern errors return LCSI_EPATTERN before anything is launched. */
