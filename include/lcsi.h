@@ -32,8 +32,17 @@
  *    call enqueues nothing.  Nothing prints, throws or aborts.
  *  - Calls are thread-safe as long as concurrent calls use distinct
  *    workspaces and outputs.
- *  - Results are deterministic: bit-identical across runs, batch sizes and
- *    query chunkings of the same rows.
+ *  - Results are deterministic: the same call on the same inputs gives the
+ *    same bits, and no result depends on how many other rows share the call:
+ *      - scores and index sets (idx_score_topk) are bit-identical across runs,
+ *        batch sizes and query chunkings of the same rows;
+ *      - sparse_attn computes each row with arithmetic fixed by top_k and by
+ *        the kind of call alone: a multi-row call (T_q > 1) takes a row's
+ *        index list in one pass, a decode call (T_q == 1) in a fixed number
+ *        of parts, ceil(top_k / 256), merged by log-sum-exp.  A row's output bits therefore do
+ *        not depend on B, and multi-row calls agree bit for bit whatever the
+ *        chunking; a decode call may differ from the same row computed inside
+ *        a multi-row call in the last bits (within the parity tolerance).
  *  - Workspaces (ws, ws_bytes) follow one rule in every call:
  *      ws == NULL, ws_bytes != NULL : query mode -- *ws_bytes receives the
  *                                     required size; nothing is launched.
@@ -188,9 +197,12 @@ int idx_score_topk(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb,
 /* Sparse attention of every query head over the rows listed in
  * idx[b*idx_sb + t*idx_st + j], j < a->top_k (the index set of this row,
  * as written by idx_score_topk).  Output to a->out in bf16.
- * ws / ws_bytes: fp32 workspace for split partial results, required only
- * when few query rows are present (B*T_q small, e.g. decode); otherwise the
- * requirement is 0 and ws may be NULL with ws_bytes NULL (workspace rule
+ * ws / ws_bytes: fp32 workspace for the partial results of a decode call
+ * (T_q == 1 with top_k > 256: each row's list runs in ceil(top_k / 256)
+ * parts of equal length, a multiple of 32 indices, on separate workgroups,
+ * then a log-sum-exp merge); the requirement is B * parts * H_q * D_v * 4
+ * bytes rounded up to 256, plus B * parts * H_q * 8 bytes.  For any other
+ * call it is 0 and ws may be NULL with ws_bytes NULL (workspace rule
  * above). */
 int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
                 int64_t idx_st, float *ws, size_t *ws_bytes, void *stream);

@@ -114,14 +114,12 @@ size_t score_ws_bytes(const lcsi_indexer *a, unsigned flags)
     return s;
 }
 
-size_t attn_ws_bytes(const lcsi_attn *a, int *splits_out = nullptr, int *split_len_out = nullptr)
+size_t attn_ws_bytes(const lcsi_attn *a, AttnPlan *plan_out = nullptr)
 {
-    int splits = 1, split_len = 0;
-    attn_plan(a->B, a->T_q, a->top_k, splits, split_len);
-    if (splits_out) *splits_out = splits;
-    if (split_len_out) *split_len_out = split_len;
-    if (splits == 1) return 0;
-    const size_t rows = (size_t)a->B * a->T_q * splits * a->H_q;
+    const AttnPlan pl = attn_plan(a->B, a->T_q, a->H_q, a->D_qk, a->top_k);
+    if (plan_out) *plan_out = pl;
+    if (pl.splits == 1) return 0;
+    const size_t rows = (size_t)a->B * a->T_q * pl.splits * a->H_q;
     const size_t o = (rows * a->D_v * sizeof(float) + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;
     return o + rows * 2 * sizeof(float);
 }
@@ -279,7 +277,10 @@ int run_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx
     aa.idx = idx;
     aa.idx_sb = idx_sb;
     aa.idx_st = idx_st;
-    attn_ws_bytes(a, &aa.splits, &aa.split_len);
+    AttnPlan pl;
+    attn_ws_bytes(a, &pl);
+    aa.splits = pl.splits;
+    aa.split_len = pl.split_len;
     if (aa.splits > 1) {
         const size_t rows = (size_t)a->B * a->T_q * aa.splits * a->H_q;
         const size_t o = (rows * a->D_v * sizeof(float) + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;

@@ -122,11 +122,16 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     // built from it are then scalar too)
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4,
               l16 = lane & 15;
-    const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+    // blockIdx.x = split + splits * (head block): when a row's heads are
+    // shared out between workgroups (decode), the workgroups that gather the
+    // same rows of one split sit `splits` apart in launch order, so with
+    // 8 splits they land on the same XCD (workgroups go round-robin over the
+    // 8 XCDs) and the second gather of a row hits that XCD's L2.
+    const int split = blockIdx.x % a.splits, hblk = blockIdx.x / a.splits, t = blockIdx.y, b = blockIdx.z;
     const int64_t p = a.q_pos0 + t;
     const int hg = wave % NWH, ds = wave / NWH;
     const int hf = ds & 1, pr = hg + NWH * (ds >> 1);  // half of S^T this wave computes; its pair
-    const int head = hg * 16 + l16;
+    const int head = (hblk * NWH + hg) * 16 + l16;
     const bool head_ok = head < a.H;
     const int j_lo = split * a.split_len;
     const int j_hi = min(a.top_k, j_lo + a.split_len);
@@ -360,14 +365,29 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 template <int DQK, int DV, bool SHARED>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
 {
-    dim3 grid(a.splits, a.T_q, a.B);
-    const int nwh = (a.H + 15) / 16;
-    if (nwh == 1)
+    dim3 grid(a.splits * a.hgroups, a.T_q, a.B);
+    const int nwh = ((a.H + 15) / 16 + a.hgroups - 1) / a.hgroups;  // 16-head groups per workgroup
+    if (a.hgroups > 1) {
+        // heads shared out between workgroups: two dim slices per head
+        // group, as in the one-workgroup kernels for more than 16 heads, so
+        // every head sees exactly the same arithmetic
+        if (nwh == 1) {
+            // (not planned for separate 576/512 K and V rows: a wave's share
+            // of the gather map would spill)
+            if constexpr (SHARED || DQK != 576)
+                hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 2, SHARED>), grid, dim3(128), 0, st, a);
+            else
+                return hipErrorInvalidValue;
+        } else {
+            hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED>), grid, dim3(256), 0, st, a);
+        }
+    } else if (nwh == 1) {
         hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 4, SHARED>), grid, dim3(256), 0, st, a);
-    else if (nwh == 2)
+    } else if (nwh == 2) {
         hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED>), grid, dim3(256), 0, st, a);
-    else
+    } else {
         hipLaunchKernelGGL((attn_kernel<DQK, DV, 4, 2, SHARED>), grid, dim3(512), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.B * a.T_q), dim3(128), 0, st, a);
@@ -376,32 +396,49 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
 
 }  // namespace
 
-#ifndef ATTN_SPLIT_TARGET
-#define ATTN_SPLIT_TARGET 256   // workgroups aimed at when few rows are present
+#ifndef ATTN_DECODE_TILES
+#define ATTN_DECODE_TILES 8     // index tiles per split of a decode row
 #endif
-#ifndef ATTN_MIN_TILES
-#define ATTN_MIN_TILES 4        // index tiles per split at least (fewer: the fp32 partials outweigh the gather)
+#ifndef ATTN_WG_TARGET
+#define ATTN_WG_TARGET 512      // workgroups a decode call aims for by sharing out heads
 #endif
 
-void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len)
+AttnPlan attn_plan(int B, int T_q, int H, int DQK, int top_k)
 {
-    const int64_t rows = (int64_t)B * T_q;
+    (void)DQK;
+    AttnPlan pl{1, 0};
     const int tiles = (top_k + TK - 1) / TK;
-    int s = 1;
-    if (rows < 256) {
-        s = (int)((ATTN_SPLIT_TARGET + rows - 1) / rows);
-        const int max_s = (tiles + ATTN_MIN_TILES - 1) / ATTN_MIN_TILES;
-        if (s > max_s) s = max_s;
-        if (s < 1) s = 1;
-    }
+    // A decode call (one query row per sequence) splits every row's index
+    // list into parts of ATTN_DECODE_TILES tiles, merged by log-sum-exp; a
+    // multi-row call runs each row in one workgroup.  Either way the parts
+    // -- and so the bits of the result -- are fixed by top_k alone for that
+    // kind of call, whatever B is.
+    const int s = T_q == 1 ? (tiles + ATTN_DECODE_TILES - 1) / ATTN_DECODE_TILES : 1;
     const int per = (tiles + s - 1) / s;
-    split_len = per * TK;
-    splits = (top_k + split_len - 1) / split_len;
+    pl.split_len = per * TK;
+    pl.splits = (top_k + pl.split_len - 1) / pl.split_len;
+    (void)B;
+    (void)H;
+    return pl;
 }
 
-hipError_t launch_attn(const AttnArgs &a, hipStream_t st)
+hipError_t launch_attn(const AttnArgs &a_in, hipStream_t st)
 {
-    const bool shared = a.v == a.k && a.v_st == a.k_st;
+    AttnArgs a = a_in;
+    // one gathered row serves K and V when V is the first D_v columns of the
+    // same rows, batch entry by batch entry
+    const bool shared = a.v == a.k && a.v_st == a.k_st && (a.v_sb == a.k_sb || a.B == 1);
+    // few rows (decode): share each row's heads out between workgroups -- no
+    // change to any head's arithmetic -- until the call has enough
+    // workgroups.  One head group per workgroup (two waves) only where a
+    // wave's gather map fits its registers: a shared KV row, or 128-wide rows.
+    a.hgroups = 1;
+    if (a.T_q == 1 && a.H > 16) {
+        const int hb = (a.H + 15) / 16;
+        const int gmax = (shared || a.DQK == 128) ? hb : hb / 2;
+        const int64_t rows = (int64_t)a.B * a.T_q;
+        while (a.hgroups < 4 && 2 * a.hgroups <= gmax && rows * a.splits * a.hgroups < ATTN_WG_TARGET) a.hgroups *= 2;
+    }
     if (a.DQK == 576 && a.DV == 512)
         return shared ? launch_attn_d<576, 512, true>(a, st) : launch_attn_d<576, 512, false>(a, st);
     if (a.DQK == 128 && a.DV == 128)

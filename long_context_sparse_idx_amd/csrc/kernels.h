@@ -94,9 +94,20 @@ struct AttnArgs {
     int64_t idx_sb, idx_st;
     int splits;               // key splits per query row (1 = write bf16 directly)
     int split_len;            // index entries per split (multiple of 32)
+    int hgroups;              // workgroups sharing one row's heads (each takes H / hgroups of them)
     float *part_o;            // [B*T_q][splits][H][DV] (splits > 1)
     float *part_ml;           // [B*T_q][splits][H][2]
 };
+
+// How sparse_attn splits each row's index list.  The split count (and so the
+// arithmetic of every row) depends only on top_k and on whether the call is a
+// decode call (T_q == 1), never on B or on the other rows of the call.
+// launch_attn may also share a row's heads out between workgroups, which
+// changes no arithmetic.
+struct AttnPlan {
+    int splits, split_len;
+};
+AttnPlan attn_plan(int B, int T_q, int H, int DQK, int top_k);
 
 bool score_use_split(const ScoreArgs &a);
 // Whether a call with these arguments can take the fused selection.
@@ -125,7 +136,6 @@ struct OverlapArgs {
     int32_t *counts;          // [B * T_q]
 };
 
-void attn_plan(int B, int T_q, int top_k, int &splits, int &split_len);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
 hipError_t launch_overlap(const OverlapArgs &a, hipStream_t st);
 

@@ -145,7 +145,8 @@ def indexer_desc(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, top_k: int, 
                  q_scale: Optional[torch.Tensor] = None) -> Indexer:
     """q [B,T_q,H,D] bf16, or fp8 e4m3 bytes (uint8 / float8_e4m3fn) with
     q_scale [B,T_q,H] fp32; k [B,T_kv,D] bf16 or fp8 e4m3 bytes with k_scale
-    [B,T_kv] fp32; w [B,T_q,H] fp32."""
+    [B,T_kv] fp32; w [B,T_q,H] fp32.  T_kv (default k.shape[1]) may name a
+    prefix of the keys, never more than k holds."""
     _inner(q, "q", 4, (torch.bfloat16,) + _FP8)
     _inner(k, "k", 3, (torch.bfloat16,) + _FP8)
     _inner(w, "w", 3, (torch.float32,))
@@ -153,15 +154,19 @@ def indexer_desc(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, top_k: int, 
     fp8 = k.dtype in _FP8
     q8 = q.dtype in _FP8
     _need(tuple(k.shape[::2]) == (B, D) and tuple(w.shape) == (B, T_q, H), "q, k, w: shapes do not agree")
+    n_kv = k.shape[1] if T_kv is None else int(T_kv)
+    _need(0 < n_kv <= k.shape[1], f"T_kv={n_kv} outside 1..{k.shape[1]} (the keys k holds)")
     if fp8:
         _need(k_scale is not None, "k_scale is required with fp8 keys")
         _inner(k_scale, "k_scale", 2, (torch.float32,))
+        _need(k_scale.shape[0] == B and k_scale.shape[1] >= n_kv, "k_scale: expected [B, >=T_kv]")
     if q8:
         _need(q_scale is not None, "q_scale is required with fp8 queries")
         _inner(q_scale, "q_scale", 3, (torch.float32,))
+        _need(tuple(q_scale.shape) == (B, T_q, H), "q_scale: expected [B, T_q, H]")
     d = Indexer()
     d.B, d.T_q, d.H_I, d.D_I, d.top_k = B, T_q, H, D, top_k
-    d.T_kv = k.shape[1] if T_kv is None else T_kv
+    d.T_kv = n_kv
     d.key_dtype = LCSI_KEY_FP8_E4M3 if fp8 else LCSI_KEY_BF16
     d.q_dtype = LCSI_Q_FP8_E4M3 if q8 else LCSI_Q_BF16
     d.q_pos0 = q_pos0
@@ -184,13 +189,21 @@ def preset_desc(B: int, T_q: int, T_kv: int, q_pos0: int, top_k: int) -> Indexer
 def attn_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, top_k: int,
               q_pos0: int, sm_scale: float, T_kv: Optional[int] = None) -> Attn:
     """q [B,T_q,H,Dqk]; k [B,T_kv,Dqk]; v [B,T_kv,Dv] (may be a column view of
-    k); out [B,T_q,H,Dv]; all bf16."""
+    k); out [B,T_q,H,Dv]; all bf16.  T_kv (default k.shape[1]) may name a
+    prefix of the keys, never more than k and v hold."""
     for t, name, dims in ((q, "q", 4), (k, "k", 3), (v, "v", 3), (out, "out", 4)):
         _inner(t, name, dims, (torch.bfloat16,))
     B, T_q, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    _need(k.shape[0] == B and k.shape[2] == Dqk, f"k: expected [{B}, T_kv, {Dqk}], got {tuple(k.shape)}")
+    _need(v.shape[0] == B and v.shape[1] == k.shape[1],
+          f"v: expected [{B}, {k.shape[1]}, Dv] like k, got {tuple(v.shape)}")
+    _need(tuple(out.shape) == (B, T_q, H, Dv), f"out: expected {(B, T_q, H, Dv)}, got {tuple(out.shape)}")
+    n_kv = k.shape[1] if T_kv is None else int(T_kv)
+    _need(0 < n_kv <= k.shape[1], f"T_kv={n_kv} outside 1..{k.shape[1]} (the rows k and v hold)")
     d = Attn()
-    d.B, d.T_q, d.H_q, d.D_qk, d.D_v, d.top_k = B, T_q, H, Dqk, v.shape[-1], top_k
-    d.T_kv = k.shape[1] if T_kv is None else T_kv
+    d.B, d.T_q, d.H_q, d.D_qk, d.D_v, d.top_k = B, T_q, H, Dqk, Dv, top_k
+    d.T_kv = n_kv
     d.sm_scale = sm_scale
     d.q_pos0 = q_pos0
     d.q, (d.q_sb, d.q_st, d.q_sh) = q.data_ptr(), q.stride()[:3]
@@ -198,6 +211,19 @@ def attn_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tens
     d.v, (d.v_sb, d.v_st) = v.data_ptr(), v.stride()[:2]
     d.out, (d.o_sb, d.o_st, d.o_sh) = out.data_ptr(), out.stride()[:3]
     return d
+
+
+def _check_idx(idx: torch.Tensor, desc, name: str = "idx"):
+    """An index tensor for rows (B, T_q) of `desc`: [B, T_q, >= top_k] int32,
+    innermost dimension contiguous."""
+    _inner(idx, name, 3, (torch.int32,))
+    _need(tuple(idx.shape[:2]) == (desc.B, desc.T_q) and idx.shape[2] >= desc.top_k,
+          f"{name}: expected [{desc.B}, {desc.T_q}, >={desc.top_k}], got {tuple(idx.shape)}")
+
+
+def _elements_from(t: torch.Tensor) -> int:
+    """int32 elements addressable from t's first element to the end of its storage."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
 
 
 # -------------------------------------------------------------------- calls
@@ -210,14 +236,15 @@ def idx_score_topk_ws_bytes(desc: Indexer, flags: int = 0) -> int:
 
 
 def idx_score_topk(desc: Indexer, idx: Optional[torch.Tensor], ws: torch.Tensor, flags: int = 0,
-                   stream=None, idx_strides: Optional[Sequence[int]] = None):
+                   stream=None):
     """Run the indexer of one F layer; idx [B,T_q,>=top_k] int32 (or a view of
     an index-cache slot), ws: score workspace (see idx_score_topk_ws_bytes)."""
     cap = ctypes.c_size_t(ws.numel() * ws.element_size())
     if idx is not None:
-        _inner(idx, "idx", 3, (torch.int32,))
-        sb, st = idx_strides if idx_strides is not None else idx.stride()[:2]
+        _check_idx(idx, desc)
+        sb, st = idx.stride()[:2]
     else:
+        _need(flags & LCSI_SCORES_ONLY, "idx is required unless flags has LCSI_SCORES_ONLY")
         sb = st = 0
     _check(lib.idx_score_topk(ctypes.byref(desc), _ptr(idx), sb, st, _ptr(ws), ctypes.byref(cap),
                               flags, _stream(stream)), "idx_score_topk")
@@ -230,10 +257,10 @@ def sparse_attn_ws_bytes(desc: Attn) -> int:
     return n.value
 
 
-def sparse_attn(desc: Attn, idx: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None,
-                idx_strides: Optional[Sequence[int]] = None):
-    _inner(idx, "idx", 3, (torch.int32,))
-    sb, st = idx_strides if idx_strides is not None else idx.stride()[:2]
+def sparse_attn(desc: Attn, idx: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None):
+    """Sparse attention of one layer over idx [B,T_q,>=top_k] int32."""
+    _check_idx(idx, desc)
+    sb, st = idx.stride()[:2]
     if ws is None:
         need = sparse_attn_ws_bytes(desc)
         ws = _ws(need, idx.device)
@@ -246,8 +273,16 @@ def sparse_attn(desc: Attn, idx: torch.Tensor, ws: Optional[torch.Tensor] = None
 def run_layer_group(pattern: Sequence[int], idx_descs: Sequence[Indexer], attn_descs: Sequence[Attn],
                     idx_cache: torch.Tensor, n_slots: int, slot_stride: int, idx_sb: int, idx_st: int,
                     ws: Optional[torch.Tensor] = None, events=None, stream=None):
-    """The F/S loop.  idx_cache: int32 device buffer holding n_slots slots."""
+    """The F/S loop.  idx_cache: int32 device buffer holding n_slots slots
+    (slot s at element s*slot_stride, row (b, t) at b*idx_sb + t*idx_st)."""
     L = len(pattern)
+    _need(idx_cache.dtype == torch.int32, "idx_cache: expected int32")
+    if attn_descs:
+        a0 = attn_descs[0]
+        last = (n_slots - 1) * slot_stride + (a0.B - 1) * idx_sb + (a0.T_q - 1) * idx_st + a0.top_k
+        _need(min(slot_stride, idx_sb, idx_st) >= 0 and last <= _elements_from(idx_cache),
+              f"idx_cache: {n_slots} slots of [{a0.B}, {a0.T_q}, {a0.top_k}] with strides "
+              f"({slot_stride}, {idx_sb}, {idx_st}) reach past its storage")
     pat = (ctypes.c_uint8 * L)(*[1 if x else 0 for x in pattern])
     nf = len(idx_descs)
     ia = (Indexer * max(nf, 1))(*idx_descs)
@@ -287,9 +322,10 @@ def layer_group_ws_bytes(pattern, idx_descs, attn_descs, idx_cache, n_slots, slo
 def idx_overlap(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
     """Per-row count of positions present in both index lists a, b
     [B, T_q, k] int32 (ascending, -1 padded); returns int32 [B, T_q]."""
+    _inner(a, "a", 3, (torch.int32,))
+    _inner(b, "b", 3, (torch.int32,))
+    _need(b.shape == a.shape, f"a, b: shapes {tuple(a.shape)} and {tuple(b.shape)} differ")
     B, T_q, k = a.shape
-    assert b.shape == a.shape and a.dtype == b.dtype == torch.int32
-    assert a.stride(2) == 1 and b.stride(2) == 1, "index rows must be contiguous"
     counts = torch.empty((B, T_q), dtype=torch.int32, device=a.device)
     _check(lib.idx_overlap(_ptr(a), a.stride(0), a.stride(1), _ptr(b), b.stride(0), b.stride(1),
                            B, T_q, k, _ptr(counts), _stream(stream)), "idx_overlap")

@@ -241,12 +241,21 @@ def call_attn(d, idx=FAKE, query=True):
 
 
 def test_attn_query_mode():
-    rc, n = call_attn(good_attn(top_k=2048))
-    assert rc == 0 and n > 0            # 32 rows, long lists: split partials are needed
-    rc, n = call_attn(good_attn(B=1, T_q=1024, q_pos0=0, T_kv=1024))
-    assert rc == 0 and n == 0           # enough rows: no workspace
+    # a decode call (one query row per sequence) with long lists: partials of
+    # ceil(top_k / 256) parts per row, whatever the batch size
+    for B in (1, 2, 32, 300):
+        rc, n = call_attn(good_attn(B=B, T_q=1, q_pos0=99, top_k=2048))
+        parts, H, Dv = 8, 32, 512
+        po = (B * parts * H * Dv * 4 + 255) // 256 * 256
+        assert rc == 0 and n == po + B * parts * H * 8, (B, n)
+    rc, n = call_attn(good_attn(B=2, T_q=1, q_pos0=99, top_k=256))
+    assert rc == 0 and n == 0           # one part: no partials
+    # multi-row calls never split, however few rows they hold
+    for B, T_q in ((2, 16), (1, 2), (1, 1024)):
+        rc, n = call_attn(good_attn(B=B, T_q=T_q, q_pos0=0, T_kv=1024, top_k=2048))
+        assert rc == 0 and n == 0, (B, T_q)
     # a workspace-free call is refused when partials are needed
-    assert call_attn(good_attn(top_k=2048), query=False)[0] == lcsi.LCSI_EWORKSPACE
+    assert call_attn(good_attn(T_q=1, q_pos0=99, top_k=2048), query=False)[0] == lcsi.LCSI_EWORKSPACE
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -354,6 +363,50 @@ def test_binding_checks_layouts_and_dtypes():
                        4, 0, 0.1)
     with pytest.raises(ValueError):
         lcsi.attn_desc(qa.float(), kv, kv[..., :512], out, 4, 0, 0.1)
+    # shapes that disagree with q would send the kernels past the buffers
+    bad_attn = [
+        dict(out=torch.zeros(B, T, 4, 128, dtype=torch.bfloat16)),          # Dv of out != Dv of v
+        dict(out=torch.zeros(B, T + 1, 4, 512, dtype=torch.bfloat16)),      # T_q of out
+        dict(out=torch.zeros(B, T, 8, 512, dtype=torch.bfloat16)),          # heads of out
+        dict(k=torch.zeros(B, T, 128, dtype=torch.bfloat16)),               # Dqk of k != Dqk of q
+        dict(k=torch.zeros(B + 1, T, 576, dtype=torch.bfloat16)),           # batch of k
+        dict(v=torch.zeros(B, T - 1, 512, dtype=torch.bfloat16)),           # rows of v != rows of k
+        dict(v=torch.zeros(B + 1, T, 512, dtype=torch.bfloat16)),           # batch of v
+        dict(T_kv=T + 1),                                                   # more keys than k holds
+        dict(T_kv=0),
+    ]
+    for over in bad_attn:
+        args = dict(q=qa, k=kv, v=kv[..., :512], out=out, T_kv=None)
+        args.update(over)
+        with pytest.raises(ValueError):
+            lcsi.attn_desc(args["q"], args["k"], args["v"], args["out"], 4, 0, 0.1, T_kv=args["T_kv"])
+    # indexer: key prefix, scale shapes
+    with pytest.raises(ValueError):
+        lcsi.indexer_desc(q, k, w, 4, 0, T_kv=T + 1)
+    k8 = torch.zeros(B, T, D, dtype=torch.uint8)
+    q8 = torch.zeros(B, T, H, D, dtype=torch.uint8)
+    with pytest.raises(ValueError):   # k_scale shorter than the keys
+        lcsi.indexer_desc(q, k8, w, 4, 0, k_scale=torch.ones(B, T - 1))
+    with pytest.raises(ValueError):   # q_scale of the wrong shape
+        lcsi.indexer_desc(q8, k8, w, 4, 0, k_scale=torch.ones(B, T), q_scale=torch.ones(B, T, H + 1))
+    d8 = lcsi.indexer_desc(q8, k8, w, 4, 0, k_scale=torch.ones(B, T), q_scale=torch.ones(B, T, H))
+    assert d8.q_dtype == lcsi.LCSI_Q_FP8_E4M3 and d8.T_kv == T
+    # index tensors: rows must match the descriptor, entries >= top_k
+    for bad_idx in (torch.zeros(B, T, 3, dtype=torch.int32), torch.zeros(B, T + 1, 4, dtype=torch.int32),
+                    torch.zeros(B + 1, T, 4, dtype=torch.int32), torch.zeros(B, T, 4, dtype=torch.int64),
+                    torch.zeros(B, 4, T, dtype=torch.int32).transpose(1, 2)):
+        with pytest.raises(ValueError):
+            lcsi.sparse_attn(a, bad_idx)
+        with pytest.raises(ValueError):
+            lcsi.idx_score_topk(d, bad_idx, torch.zeros(16))
+    with pytest.raises(ValueError):   # no indices and not scores-only
+        lcsi.idx_score_topk(d, None, torch.zeros(16))
+    # an index cache too small for its slots
+    small = torch.zeros(2 * B * T * 4 - 1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        lcsi.run_layer_group([1, 0], [d], [a, a], small, 2, B * T * 4, T * 4, 4)
+    with pytest.raises(ValueError):
+        lcsi.idx_overlap(torch.zeros(B, T, 4, dtype=torch.int32), torch.zeros(B, T, 5, dtype=torch.int32))
 
 
 def test_binding_refuses_to_load_without_the_library(tmp_path):

@@ -11,6 +11,8 @@ queries + per-(token, head) scale on fp8 MFMA) are covered, with ragged
 tails."""
 import dataclasses
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -112,7 +114,7 @@ def check_rows(T_q):
 def test_score_integer_exact(shape, fmt):
     B, T_q, T_kv, q_pos0, H, D, k = shape
     log(f"[score-int] shape={shape} fmt={fmt}")
-    seed = hash(shape) % 1000 + FORMATS.index(fmt)
+    seed = zlib.crc32(repr(shape).encode()) % 1000 + FORMATS.index(fmt)
     qf, kf, w = int_inputs(B, T_q, T_kv, H, D, seed=seed)
     x = encode(fmt, qf, kf, B, T_q, T_kv, H, torch.Generator().manual_seed(seed + 7))
     S, idx = gpu_indexer(dev(x, "q"), dev(x, "k"), w.cuda(), k, q_pos0, k_scale=dev(x, "k_scale"),

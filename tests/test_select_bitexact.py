@@ -3,6 +3,8 @@ byte-identical to the oracle's selection: same positions, ascending, same
 -1 padding.  Rows cover every path of the kernel: n <= k, whole row in LDS,
 the sampled-threshold pass, and the exact streaming fallback (heavy ties,
 all-equal rows, +-0, monotone rows)."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -71,7 +73,9 @@ def rows(rng, B, T_q, T_kv, kind):
 ])
 def test_select_bitexact(kind, shape):
     B, T_q, T_kv, q_pos0, k = shape
-    rng = np.random.default_rng(hash((kind,) + shape) % (2 ** 32))
+    # (a seed that does not depend on the interpreter's string hashing, so a
+    # failing case can be rerun from its log line)
+    rng = np.random.default_rng(zlib.crc32(repr((kind,) + shape).encode()))
     S = rows(rng, B, T_q, T_kv, kind)
     compare(S, B, T_q, T_kv, q_pos0, k, kind)
 
