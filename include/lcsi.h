@@ -73,6 +73,7 @@ extern "C" {
 #define LCSI_EPATTERN -4     /* layer pattern starts with S, or #F != number of indexer descriptors */
 #define LCSI_EALIGN -5       /* a base pointer or stride breaks the alignment rules */
 #define LCSI_EHIP -6         /* a kernel launch or event record returned a HIP error */
+#define LCSI_ESCRATCH -7     /* sparse_attn_noalloc: the call needs more than the static scratch */
 
 /* ------------------------------------------------------------ key dtypes */
 #define LCSI_KEY_BF16 0
@@ -206,6 +207,23 @@ int idx_score_topk(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb,
  * above). */
 int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
                 int64_t idx_st, float *ws, size_t *ws_bytes, void *stream);
+
+/* sparse_attn without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, kernels and results as sparse_attn;
+ * the partial results of a decode call go to a static device scratch of
+ * LCSI_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (looked up on the first call per device).  A call
+ * whose sparse_attn workspace requirement exceeds it returns LCSI_ESCRATCH
+ * (at H_q = 64, D_v = 512, top_k = 2048: up to 45 sequences) and launches
+ * nothing; LCSI_EINVAL also when `stream` belongs to another device than the
+ * current one.  The call allocates nothing.  Every call on one GPU uses that
+ * GPU's one scratch: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller; calls in order
+ * on one stream are safe. */
+#define LCSI_NOALLOC_SCRATCH_BYTES (48u << 20)
+int sparse_attn_noalloc(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
+                        int64_t idx_st, void *stream);
 
 /* The F/S layer loop over L layers (one conditional per layer):
  *   for l in 0..L-1:

@@ -5,8 +5,19 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "lcsi.h"
+
+// Device scratch of sparse_attn_noalloc: the partial results of a decode
+// call, held in a file-scope array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in):
+// the device address of each GPU's copy comes from hipGetSymbolAddress,
+// taken once per device with that device current (scratch_address below),
+// and only that address reaches the kernels.
+static __device__ __align__(256) uint8_t scratch[LCSI_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -290,6 +301,32 @@ int run_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx
     return launch_attn(aa, s) == hipSuccess ? LCSI_OK : LCSI_EHIP;
 }
 
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_dev[MAX_DEVICES];  // device address of `scratch` per device, guarded by scratch_mu
+
+// The address of the current device's scratch, looked up on the first call
+// for that device.  The stream (NULL: the current device's null stream) must
+// belong to the current device.
+int scratch_address(hipStream_t s, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return LCSI_EHIP;
+    if (s) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return LCSI_EHIP;
+        if ((int)sdev != dev) return LCSI_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LCSI_EHIP;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return LCSI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,6 +358,18 @@ int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t 
     rc = workspace_rule(ws, ws_bytes, attn_ws_bytes(a));
     if (rc) return rc < 0 ? rc : LCSI_OK;
     return run_attn(a, idx, idx_sb, idx_st, ws, (hipStream_t)stream);
+}
+
+int sparse_attn_noalloc(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx_st, void *stream)
+{
+    int rc = check_attn(a);
+    if (rc) return rc;
+    if ((rc = check_idx_out(idx, idx_sb, idx_st))) return rc;
+    const size_t need = attn_ws_bytes(a);
+    if (need > (size_t)LCSI_NOALLOC_SCRATCH_BYTES) return LCSI_ESCRATCH;
+    void *ws = nullptr;
+    if (need && (rc = scratch_address((hipStream_t)stream, &ws))) return rc;
+    return run_attn(a, idx, idx_sb, idx_st, (float *)ws, (hipStream_t)stream);
 }
 
 int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args, int n_idx_args,
@@ -406,6 +455,7 @@ const char *lcsi_strerror(int code)
     case LCSI_EPATTERN: return "invalid F/S layer pattern";
     case LCSI_EALIGN: return "misaligned pointer or stride";
     case LCSI_EHIP: return "HIP launch error";
+    case LCSI_ESCRATCH: return "call needs more than the library's static scratch (sparse_attn_noalloc)";
     default: return "unknown status";
     }
 }

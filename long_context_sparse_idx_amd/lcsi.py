@@ -24,6 +24,7 @@ LCSI_EWORKSPACE = -3
 LCSI_EPATTERN = -4
 LCSI_EALIGN = -5
 LCSI_EHIP = -6
+LCSI_ESCRATCH = -7
 LCSI_KEY_BF16 = 0
 LCSI_KEY_FP8_E4M3 = 1
 LCSI_Q_BF16 = 0
@@ -32,8 +33,10 @@ LCSI_SCORES_PRESET = 1
 LCSI_SCORES_ONLY = 2
 LCSI_UNFUSED = 4
 LCSI_MAX_TOPK = 2048
+LCSI_NOALLOC_SCRATCH_BYTES = 48 << 20
 
-EXPORTED = ("idx_score_topk", "sparse_attn", "run_layer_group", "idx_overlap", "lcsi_score_ld", "lcsi_strerror")
+EXPORTED = ("idx_score_topk", "sparse_attn", "sparse_attn_noalloc", "run_layer_group", "idx_overlap",
+            "lcsi_score_ld", "lcsi_strerror")
 
 
 class LcsiError(RuntimeError):
@@ -78,6 +81,8 @@ def _load():
     lib.idx_score_topk.restype = i32
     lib.sparse_attn.argtypes = [ctypes.POINTER(Attn), p, i64, i64, p, sz, p]
     lib.sparse_attn.restype = i32
+    lib.sparse_attn_noalloc.argtypes = [ctypes.POINTER(Attn), p, i64, i64, p]
+    lib.sparse_attn_noalloc.restype = i32
     lib.run_layer_group.argtypes = [i32, p, ctypes.POINTER(Indexer), i32, ctypes.POINTER(Attn), p, i32,
                                     i64, i64, i64, p, sz, p, p]
     lib.run_layer_group.restype = i32
@@ -268,6 +273,15 @@ def sparse_attn(desc: Attn, idx: torch.Tensor, ws: Optional[torch.Tensor] = None
     _check(lib.sparse_attn(ctypes.byref(desc), _ptr(idx), sb, st, _ptr(ws),
                            ctypes.byref(cap) if cap is not None else None, _stream(stream)),
            "sparse_attn")
+
+
+def sparse_attn_noalloc(desc: Attn, idx: torch.Tensor, stream=None):
+    """sparse_attn with the library's static device scratch instead of a
+    workspace (nothing is allocated, here or in the library)."""
+    _check_idx(idx, desc)
+    sb, st = idx.stride()[:2]
+    _check(lib.sparse_attn_noalloc(ctypes.byref(desc), _ptr(idx), sb, st, _stream(stream)),
+           "sparse_attn_noalloc")
 
 
 def run_layer_group(pattern: Sequence[int], idx_descs: Sequence[Indexer], attn_descs: Sequence[Attn],

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lcsi.strerror(code)
     assert lcsi.strerror(-99) == "unknown status"
 
@@ -122,6 +122,21 @@ def test_fused_pass_needs_a_row_longer_than_the_slots(last_row_keys, fused):
     # fewer rows (the split-key kernel scores them): never fused
     rc, n = call_idx(good_indexer(**dict(d, B=1)), sb=T_q * 8)
     assert rc == 0 and n == n_u // 2
+
+
+def test_noalloc_refuses_calls_beyond_its_scratch():
+    """Checked on the host before anything is launched: a decode call whose
+    partials exceed the static scratch returns LCSI_ESCRATCH; bad
+    descriptors fail as for sparse_attn."""
+    big = good_attn(B=64, T_q=1, H_q=64, q_pos0=99, top_k=2048)   # 64 * 8 * 64 * 2 KB > 48 MiB
+    rc = lcsi.lib.sparse_attn_noalloc(ctypes.byref(big), ctypes.c_void_p(FAKE), 2048, 2048, None)
+    assert rc == lcsi.LCSI_ESCRATCH
+    assert "scratch" in lcsi.strerror(rc)
+    bad = good_attn(T_q=1, q_pos0=99, top_k=0)
+    assert lcsi.lib.sparse_attn_noalloc(ctypes.byref(bad), ctypes.c_void_p(FAKE), 8, 8, None) == lcsi.LCSI_EINVAL
+    ok = good_attn(T_q=1, q_pos0=99, top_k=2048)
+    assert lcsi.lib.sparse_attn_noalloc(ctypes.byref(ok), None, 8, 8, None) == lcsi.LCSI_EINVAL
+    assert lcsi.lib.sparse_attn_noalloc(None, ctypes.c_void_p(FAKE), 8, 8, None) == lcsi.LCSI_EINVAL
 
 
 @pytest.mark.parametrize("field,value,code", [
