@@ -10,16 +10,23 @@ Headline metric: indexer + top-k prefill query-tok/s at 200K context =
 chunks of the F layer's score + select kernels, timed with HIP events that
 run_layer_group records on the launch stream.  The JSON line also carries the
 whole-path rate, the FSSS vs all-F speedup (one all-F pass after the timed
-steps), the score kernel's MFMA roofline and the CPU oracle's rate on a
-bounded sample of rows.
+steps), the score kernel's MFMA roofline (and its fraction of the measured
+matrix-core ceiling), the HBM traffic of the score, select and attention
+kernels from the committed counter runs, and the CPU oracle's rate on a
+bounded sample of rows.  After the headline the decode workloads at 131K and
+1M context and the 1M prefill chunk are timed against their all-F patterns
+(steps timed back to back without per-layer events; one more step with
+events gives the per-kernel split).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                    [--no-allf] [--no-ceilings] [--no-secondary]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -37,25 +44,35 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+SECONDARY = ("decode131k", "decode1m", "prefill1m")
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "hbm_counters.json")
+CSRC = os.path.join(ROOT, "long_context_sparse_idx_amd", "csrc")
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def score_traffic(wl):
-    """HBM bytes per score launch from the committed counter runs, or None
-    when the score kernel source changed since they were taken."""
-    import hashlib
+def source_sha(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_entry(workload: str, kernel_prefix: str):
+    """The committed FETCH_SIZE / WRITE_SIZE entry of a kernel (HBM bytes per
+    launch), or None when there is none for this workload or a source it was
+    taken from has changed since."""
     try:
-        with open(os.path.join(ROOT, "profiles", "score_traffic.json")) as f:
-            t = json.load(f)
-        with open(os.path.join(ROOT, "long_context_sparse_idx_amd", "csrc", "score.hip"), "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()
+        with open(COUNTERS_JSON) as f:
+            doc = json.load(f)
     except OSError:
         return None
-    if t.get("source_sha256") != h or t.get("workload") != wl.name:
-        return None
-    return t["bytes_per_launch"]
+    for e in doc.get("entries", []):
+        if e["workload"] != workload or not e["kernel"].startswith(kernel_prefix):
+            continue
+        if all(source_sha(s) == h for s, h in e["sources"].items()):
+            return e
+    return None
 
 
 def cpu_baseline(path: Workload, max_rows: int | None = None):
@@ -111,10 +128,55 @@ def cpu_baseline(path: Workload, max_rows: int | None = None):
                       f"{dt:.1f} s wall on {threads} threads"}
 
 
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def mfma_ceiling():
+    """The score kernel's matrix-core instruction stream with nothing else
+    (libceiling.so): B operands from registers (mode 0) and from LDS with the
+    score kernel's reads (mode 1), on N(0,1)/8 bf16 operands.  TFLOP/s."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_idx_amd", "libceiling.so"))
+    lib.lcsi_ceiling_data_elems.restype = ctypes.c_size_t
+    lib.lcsi_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lib.lcsi_ceiling_mfma.restype = ctypes.c_int
+    n = lib.lcsi_ceiling_data_elems()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    data = (torch.randn(n, device="cuda", generator=g) / 8).to(torch.bfloat16)
+    n_wg, blocks = 2048, 1024
+    out = torch.empty(n_wg * 8, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for mode in (0, 1):
+        def launch():
+            rc = lib.lcsi_ceiling_mfma(ctypes.c_void_p(data.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                       n_wg, blocks, mode, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"lcsi_ceiling_mfma: {rc}")
+        for _ in range(2):
+            launch()
+        torch.cuda.synchronize()
+        e0, e1 = _events(2)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        flops = n_wg * 8 * blocks * 16 * 32768.0 * reps
+        res[("mfma_only_regs" if mode == 0 else "mfma_lds_reads") + "_TFLOPs"] = round(
+            flops / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+    del data, out
+    return res
+
+
 def measured_ceilings():
     """Practical ceilings on this GPU, for context beside the datasheet peaks:
-    a library bf16 GEMM (8192^3, entries N(0,1)/8 like the indexer inputs) and
-    a 4 GiB device-to-device copy.  Both run after the timed region."""
+    a library bf16 GEMM (8192^3, entries N(0,1)/8 like the indexer inputs),
+    the score kernel's MFMA stream alone (libceiling.so), a 4 GiB
+    device-to-device copy and a 4 GiB read-only reduction.  All run after the
+    timed region."""
     g = torch.Generator(device="cuda").manual_seed(0)
     n = 8192
     a = (torch.randn(n, n, device="cuda", generator=g) / 8).to(torch.bfloat16)
@@ -122,7 +184,7 @@ def measured_ceilings():
     for _ in range(3):
         torch.matmul(a, b)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = _events(2)
     reps = 20
     e0.record()
     for _ in range(reps):
@@ -131,6 +193,8 @@ def measured_ceilings():
     torch.cuda.synchronize()
     gemm = 2 * n ** 3 * reps / (e0.elapsed_time(e1) / 1e3) / 1e12
     del a, b
+    res = {"bf16_gemm_8192_TFLOPs": round(gemm, 1), "bf16_gemm_frac_of_peak": round(gemm / PEAK_BF16_TFLOPS, 4)}
+    res.update(mfma_ceiling())
     src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -141,10 +205,90 @@ def measured_ceilings():
     e1.record()
     torch.cuda.synchronize()
     copy = 2 * src.numel() * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del src, dst
+    del dst
+    s = src.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        s = src.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read = src.numel() * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, s
     torch.cuda.empty_cache()
-    return {"bf16_gemm_8192_TFLOPs": round(gemm, 1), "bf16_gemm_frac_of_peak": round(gemm / PEAK_BF16_TFLOPS, 4),
-            "copy_4GiB_GBps": round(copy, 1), "copy_frac_of_peak": round(copy / PEAK_HBM_GBS, 4)}
+    res.update({"copy_4GiB_GBps": round(copy, 1), "copy_frac_of_peak": round(copy / PEAK_HBM_GBS, 4),
+                "read_4GiB_sum_GBps": round(read, 1), "read_frac_of_peak": round(read / PEAK_HBM_GBS, 4)})
+    return res
+
+
+def split_ms(events, nchunk, L):
+    """Score / select / attention ms of one step from run_layer_group's
+    per-layer events."""
+    sc = se = at = 0.0
+    for c in range(nchunk):
+        ev = events[c]
+        for l in range(L):
+            sc += ev[4 * l].elapsed_time(ev[4 * l + 1])
+            se += ev[4 * l + 1].elapsed_time(ev[4 * l + 2])
+            at += ev[4 * l + 2].elapsed_time(ev[4 * l + 3])
+    return sc, se, at
+
+
+def time_steps(path, plan, steps, warmup):
+    """ms per step over `steps` back-to-back steps (no per-layer events), and
+    one more step with per-layer events: (ms/step, score ms, select ms,
+    attention ms)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        path.step(plan)
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record(stream)
+    for _ in range(steps):
+        path.step(plan)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    L = len(plan[0])
+    nchunk = len(plan[1])
+    ev = [_events(4 * L) for _ in range(nchunk)]
+    path.step(plan, ev)
+    torch.cuda.synchronize()
+    sc, se, at = split_ms(ev, nchunk, L)
+    return ms, sc, se, at
+
+
+def secondary(name: str, steps: int, warmup: int):
+    """One of the other workloads, its layer pattern against all-F."""
+    wl = inputs.WORKLOADS[name]
+    L = wl.n_layers
+    t0 = time.time()
+    path = Workload(wl, f_layers=range(L), log=log)
+    pat = path.plan(wl.pattern)
+    ms, sc, se, at = time_steps(path, pat, steps, warmup)
+    allf = path.plan(tuple(1 for _ in range(L)))
+    ms_f, sc_f, se_f, at_f = time_steps(path, allf, steps, warmup)
+    n_tok = wl.B * wl.n_q
+    unit = "tok/s" if wl.T_q == 1 else "query-tok/s"
+    out = {
+        "pattern": "".join("F" if f else "S" for f in wl.pattern),
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        unit: round(n_tok / (ms / 1e3), 1),
+        "indexer_" + unit: round(n_tok / ((sc + se) / 1e3), 1),
+        "allF_ms_per_step": round(ms_f, 4),
+        "speedup_vs_allF": round(ms_f / ms, 3),
+        "split_ms_one_evented_step": {"score": round(sc, 4), "select": round(se, 4), "attention": round(at, 4),
+                                      "allF_score": round(sc_f, 4), "allF_select": round(se_f, 4),
+                                      "allF_attention": round(at_f, 4)},
+        "indexer_share_allF": round((sc_f + se_f) / (sc_f + se_f + at_f), 3),
+        "indexer_share_pattern": round((sc + se) / (sc + se + at), 3),
+    }
+    log(f"[bench] {name}: {ms:.3f} ms/step ({out[unit]:.0f} {unit}), all-F {ms_f:.3f} ms, "
+        f"x{out['speedup_vs_allF']} ({time.time() - t0:.1f} s)")
+    del path
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -156,9 +300,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-allf", action="store_true", help="skip the all-F comparison pass")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the library GEMM / device copy ceiling measurements")
+                    help="skip the library GEMM / MFMA loop / copy / read ceiling measurements")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the decode 131K, decode 1M and prefill 1M timings after the headline")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run one plain 1 GiB device-to-device copy first (reference for HBM counters)")
+                    help="run one plain 1 GiB device copy and one 1 GiB read-only reduction first "
+                         "(references of known size for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
@@ -172,8 +319,10 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)          # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
-        del src, dst
-        log("[bench] calibration copy of 1 GiB done")
+        s = src.sum()           # reads 1 GiB, writes a few bytes
+        torch.cuda.synchronize()
+        del src, dst, s
+        log("[bench] calibration: 1 GiB copy and 1 GiB read-only sum done")
     wl = inputs.WORKLOADS[args.workload]
     path = Workload(wl, f_layers=range(wl.n_layers) if not args.no_allf else None, log=log)
     pattern = wl.pattern
@@ -181,7 +330,7 @@ def main():
     plans = plan[1]
     L = wl.n_layers
     nchunk = len(plans)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] for _ in range(nchunk)]
+    events = [_events(4 * L) for _ in range(nchunk)]
     stream = torch.cuda.current_stream()
 
     for i in range(args.warmup):
@@ -189,7 +338,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start, end = _events(2)
     step_ms, idx_ms, score_ms, select_ms, attn_ms = [], [], [], [], []
     torch.cuda.synchronize()
     start.record(stream)
@@ -198,13 +347,7 @@ def main():
         s0.record(stream)
         path.step(plan, events)
         torch.cuda.synchronize()
-        sc = se = at = 0.0
-        for c in range(nchunk):
-            ev = events[c]
-            for l in range(L):
-                sc += ev[4 * l].elapsed_time(ev[4 * l + 1])
-                se += ev[4 * l + 1].elapsed_time(ev[4 * l + 2])
-                at += ev[4 * l + 2].elapsed_time(ev[4 * l + 3])
+        sc, se, at = split_ms(events, nchunk, L)
         step_ms.append(s0.elapsed_time(events[-1][-1]))
         score_ms.append(sc)
         select_ms.append(se)
@@ -228,6 +371,7 @@ def main():
     n_f = sum(pattern)
     score_s = float(np.mean(score_ms)) / 1e3
     kdt = "fp8xfp8" if wl.q_fp8 else ("fp8" if wl.key_fp8 else "bf16")
+
     # the fused candidate pass (prefill kernel, 16+ heads, a row longer than
     # its candidate slots): the library plans it when its workspace needs
     # the slots; chunks of shorter rows run unfused
@@ -236,11 +380,13 @@ def main():
     n_fused = sum(plan_fused(p[3][0]) for p in plans)
     fused = n_fused > 0
     peak = PEAK_FP8_TFLOPS if wl.q_fp8 else PEAK_BF16_TFLOPS
+    score_launch_ms = float(np.mean(score_ms)) / (nchunk * n_f)
+    score_counters = counter_entry(wl.name, "score_prefill_kernel" if wl.T_q > 1 else "score_splitkey_kernel")
     if wl.T_q > 1:
         achieved = pairs * flops_per_pair * n_f / score_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": score_traffic(wl),
+                    "traffic": score_counters["bytes_per_launch"] if score_counters else None,
                     "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}{',fused' if fused else ''}>"}
     else:
         # keys (+ fp8 scale) read once per sequence, queries and weights, score row written
@@ -250,21 +396,33 @@ def main():
         achieved = sc_bytes / score_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": score_traffic(wl),
+                    "traffic": score_counters["bytes_per_launch"] if score_counters else None,
                     "kernel": f"score_splitkey_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
     roofline["launches_per_step"] = nchunk * n_f
     if fused:
         roofline["fused_launches_per_step"] = n_fused * n_f
-    roofline["avg_launch_ms"] = round(float(np.mean(score_ms)) / (nchunk * n_f), 4)
-    # select: HBM-bound; algorithmic bytes = read each causal score once + write k indices
-    # (after the fused pass the selection reads candidates, not score rows:
-    # no figure then)
-    sel_bytes = (pairs * 4 + n_q_total * wl.top_k * 4) * n_f
-    sel_gbs = None if fused else round(sel_bytes / (float(np.mean(select_ms)) / 1e3) / 1e9, 1)
+    roofline["avg_launch_ms"] = round(score_launch_ms, 4)
     # attention: bytes of the gathered KV rows (576 x bf16 per selected index) + Q + O
     sel_per_row = sum(min(wl.top_k, p + 1) for p in range(wl.q_pos0, wl.q_pos0 + wl.n_q)) * wl.B
     attn_bytes = (sel_per_row * wl.D_qk * 2 + n_q_total * wl.H_q * (wl.D_qk + wl.D_v) * 2) * L
     attn_gbs = attn_bytes / (float(np.mean(attn_ms)) / 1e3) / 1e9
+
+    # measured HBM traffic (committed FETCH_SIZE / WRITE_SIZE runs of the
+    # same sources) over the launch times measured in this run
+    def hbm(entry, launch_ms):
+        if entry is None:
+            return None
+        gbs = entry["bytes_per_launch"] / (launch_ms / 1e3) / 1e9
+        return {"kernel": entry["kernel"], "bytes_per_launch": entry["bytes_per_launch"],
+                "launch_ms_this_run": round(launch_ms, 4), "GBps": round(gbs, 1),
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    hbm_block = {
+        "source": "bytes per launch from profiles/hbm_counters.json (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE, "
+                  "copy- and read-calibrated, same kernel sources); launch times measured in this run",
+        "score": hbm(score_counters, score_launch_ms),
+        "select": hbm(counter_entry(wl.name, "select_"), float(np.mean(select_ms)) / (nchunk * n_f)),
+        "attention": hbm(counter_entry(wl.name, "attn_kernel"), float(np.mean(attn_ms)) / (nchunk * L)),
+    }
 
     extra = {}
     if not args.no_allf:
@@ -272,8 +430,8 @@ def main():
         plan_f = path.plan(allf)
         path.step(plan_f)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev_f = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * L)] for _ in range(nchunk)]
+        e0, e1 = _events(2)
+        ev_f = [_events(4 * L) for _ in range(nchunk)]
         e0.record(stream)
         path.step(plan_f, ev_f)
         e1.record(stream)
@@ -286,14 +444,25 @@ def main():
         extra["indexer_share_fsss"] = round(idx_mean / float(np.mean(step_ms)), 3)
         log(f"[bench] all-F pass: {allf_ms:.1f} ms")
 
-    if not args.no_ceilings:
-        extra["measured_ceilings"] = measured_ceilings()
-        log(f"[bench] ceilings: {extra['measured_ceilings']}")
-
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(path)
         log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} ({cpu['sample']})")
+    del path, plan, plans, events
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary and wl.name == "prefill200k":
+        sec_steps = min(args.steps, 20)
+        for name in SECONDARY:
+            st, wu = (min(sec_steps, 4), 1) if name == "prefill1m" else (sec_steps, max(args.warmup, 2))
+            extra[name] = secondary(name, st, wu)
+
+    if not args.no_ceilings:
+        extra["measured_ceilings"] = measured_ceilings()
+        if wl.T_q > 1 and not wl.q_fp8:
+            ceil = extra["measured_ceilings"]["mfma_lds_reads_TFLOPs"]
+            roofline["frac_of_mfma_lds_ceiling"] = round(roofline["achieved"] / ceil, 4)
+        log(f"[bench] ceilings: {extra['measured_ceilings']}")
 
     line = {
         "metric": "indexer+top-k prefill query-tok/s at 200K ctx" if wl.name == "prefill200k"
@@ -319,9 +488,10 @@ def main():
         "ms": {"score": round(float(np.mean(score_ms)), 3), "select": round(float(np.mean(select_ms)), 3),
                "attention": round(float(np.mean(attn_ms)), 3), "indexer": round(idx_mean, 3),
                "step_events": round(float(np.mean(step_ms)), 3)},
-        "select_algorithmic_GBps": sel_gbs,
-        "select_input": "fused candidates" if fused else "score rows",
+        "hbm": hbm_block,
         "attention_algorithmic_GBps": round(attn_gbs, 1),
+        "attention_algorithmic_note": "gathered KV rows + Q + O per launch over its time; can exceed the "
+                                      "HBM peak where rows repeat within the Infinity Cache (see hbm)",
         **extra,
     }
     print(json.dumps(line), flush=True)

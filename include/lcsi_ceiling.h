@@ -1,0 +1,40 @@
+/*
+ * lcsi_ceiling.h -- measurement helper of the benchmark, in its own library
+ * (libceiling.so), not a step of the method: the practical matrix-core
+ * ceiling of the indexer score kernel on this GPU.
+ *
+ * lcsi_ceiling_mfma launches n_wg workgroups of 8 waves (two per SIMD, as
+ * the score kernel) that each issue `blocks` times the score kernel's block
+ * of 16 v_mfma_f32_32x32x16_bf16 (two 32-row tiles x 8 k-steps of 16 dims,
+ * two accumulator chains) and nothing else: no epilogue, no stores but one
+ * float per wave, no key traffic from memory.
+ *   data   device bf16, lcsi_ceiling_data_elems() values (the query rows, then
+ *          256 key rows of 128 dims); the caller fills it with the value
+ *          distribution under test (the benchmark: N(0,1)/8, the indexer's).
+ *   out    device fp32, n_wg * 8 values (one per wave), written.
+ *   mode   0: B operands in registers, changing block by block (4 sets);
+ *          1: B operands read from two key tiles staged once in LDS, with
+ *          the score kernel's LDS reads.
+ *   blocks a multiple of 4, at least 4.
+ * Work per launch: n_wg * 8 * blocks * 16 * 32768 flop.  Asynchronous on
+ * `stream` (a hipStream_t as void*).  Returns 0, -1 for a bad argument, -5
+ * for a misaligned pointer (data 16 bytes, out 4), -6 if the launch failed.
+ */
+#ifndef LCSI_CEILING_H
+#define LCSI_CEILING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+size_t lcsi_ceiling_data_elems(void);
+int lcsi_ceiling_mfma(const uint16_t *data, float *out, int n_wg, int blocks, int mode, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCSI_CEILING_H */

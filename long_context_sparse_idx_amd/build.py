@@ -18,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblcsi.so")
 SOURCES = ["score.hip", "select.hip", "attn.hip", "overlap.hip", "api.hip"]
+CEILING_SOURCES = ["ceiling.hip"]
+CEILING_LIB = os.path.join(PKG, "libceiling.so")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -42,18 +44,25 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     r = subprocess.run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Build liblcsi.so (the library) and libceiling.so (the benchmark's
+    matrix-core ceiling helper)."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES + CEILING_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

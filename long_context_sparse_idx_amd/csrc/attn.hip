@@ -333,8 +333,11 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
 }
 
 // Combine the per-split partial results of one (query row, head):
-// O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s.
-// One workgroup per (head, row); thread i owns output dims 4i .. 4i+3.
+// O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s,
+// summed over s in ascending order.  One workgroup per (head, row); thread i
+// owns output dims 4i .. 4i+3.  S = the split count, fixed at compile time so
+// that every partial of a thread is loaded before the first is used.
+template <int S>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 {
     const int h = blockIdx.x;
@@ -342,24 +345,50 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
     const int b = (int)(row / a.T_q), t = (int)(row % a.T_q);
     const int d = 4 * threadIdx.x;
     if (d >= a.DV) return;
+    float ms[S], ls[S];
+    f32x4 os[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t r = (row * S + s) * a.H + h;
+        const f32x2 ml = *reinterpret_cast<const f32x2 *>(a.part_ml + r * 2);
+        ms[s] = ml[0];
+        ls[s] = ml[1];
+        os[s] = *reinterpret_cast<const f32x4 *>(a.part_o + r * a.DV + d);
+    }
     float M = -__builtin_inff();
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[((row * a.splits + s) * a.H + h) * 2]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ms[s]);
     f32x4 o{0, 0, 0, 0};
     float L = 0.f;
     if (M != -__builtin_inff()) {
-        for (int s = 0; s < a.splits; ++s) {
-            const int64_t r = (row * a.splits + s) * a.H + h;
-            const float ms = a.part_ml[r * 2];
-            if (ms == -__builtin_inff()) continue;
-            const float f = __builtin_amdgcn_exp2f(ms - M);
-            L += a.part_ml[r * 2 + 1] * f;
-            o += *reinterpret_cast<const f32x4 *>(a.part_o + r * a.DV + d) * f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            if (ms[s] == -__builtin_inff()) continue;
+            const float f = __builtin_amdgcn_exp2f(ms[s] - M);
+            L += ls[s] * f;
+            o += os[s] * f;
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     o *= inv;
     uint16_t *op = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + d;
     *reinterpret_cast<u32x2 *>(op) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+
+hipError_t launch_merge(const AttnArgs &a, hipStream_t st)
+{
+    const dim3 grid(a.H, a.B * a.T_q), block(128);
+    switch (a.splits) {
+    case 2: hipLaunchKernelGGL(attn_merge_kernel<2>, grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL(attn_merge_kernel<3>, grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(attn_merge_kernel<4>, grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL(attn_merge_kernel<5>, grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL(attn_merge_kernel<6>, grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL(attn_merge_kernel<7>, grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(attn_merge_kernel<8>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;  // (a decode call has at most 2048 / 256 parts)
+    }
+    return hipGetLastError();
 }
 
 template <int DQK, int DV, bool SHARED>
@@ -390,8 +419,7 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H, a.B * a.T_q), dim3(128), 0, st, a);
-    return hipGetLastError();
+    return launch_merge(a, st);
 }
 
 }  // namespace

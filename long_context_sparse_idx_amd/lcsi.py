@@ -15,7 +15,9 @@ from typing import Optional, Sequence
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcsi.so")
+# LCSI_LIB names another build of the same library to load instead (the
+# sanitizer test points it at a host-ASan build); never a fallback.
+_LIB_PATH = os.environ.get("LCSI_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcsi.so")
 
 LCSI_OK = 0
 LCSI_EINVAL = -1

@@ -10,6 +10,13 @@ import torch
 SCORE_RTOL = 1e-2
 FLOOR = 1e-3
 ATTN_ATOL = 2e-2
+# Row-relative diagnostic of attention outputs, asserted beside ATTN_ATOL:
+# max |gpu - oracle| over a row's heads and dims divided by max |oracle| of
+# the row.  Leaving out one 32-index tile of a 2048-index set moves a row by
+# 0.08 - 0.16 of its largest output on N(0,1) inputs (shown with the oracle
+# alone in tests/test_tolerance_power.py), so a bound of 0.04 catches it while
+# the bf16 rounding of the outputs and of the softmax weights stays far below.
+ATTN_ROW_REL = 0.04
 
 
 def log(*a):
@@ -60,3 +67,15 @@ def check_index_sets(g_idx: np.ndarray, r_idx: np.ndarray, r_row: np.ndarray, k:
     for s in diff:
         assert abs(rr[s] - vk) <= tol, f"{what}: index {s} score {rr[s]} vs k-th {vk}"
     return len(diff)
+
+
+def attn_row_rel(g_bits: np.ndarray, r_bits: np.ndarray) -> np.ndarray:
+    """Per-row attention diagnostic: the last two axes (heads, dims) form a
+    row; returns max |g - r| / max |r| for every row (0 for an all-zero
+    oracle row that the GPU matches)."""
+    g = bf16_to_f64(g_bits)
+    r = bf16_to_f64(r_bits)
+    lead = r.shape[:-2]
+    d = np.abs(g - r).reshape(*lead, -1).max(-1)
+    m = np.abs(r).reshape(*lead, -1).max(-1)
+    return np.where(m > 0, d / np.where(m > 0, m, 1.0), d)

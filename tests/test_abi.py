@@ -435,6 +435,7 @@ def test_binding_refuses_to_load_without_the_library(tmp_path):
     code = ("import sys; sys.path.insert(0, %r)\n"
             "try:\n    import pkg_no_lib.lcsi\nexcept ImportError as e:\n    print('refused:', e)\n"
             "else:\n    print('loaded')\n") % str(tmp_path)
-    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    env = {k: v for k, v in os.environ.items() if k != "LCSI_LIB"}
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("refused:") and "no fallback" in r.stdout, r.stdout

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import ATTN_ATOL, bf16_to_f64, bits, log
+from helpers import ATTN_ATOL, ATTN_ROW_REL, attn_row_rel, bf16_to_f64, bits, log
 from long_context_sparse_idx_amd import lcsi
 
 pytestmark = pytest.mark.gpu
@@ -92,9 +92,12 @@ def test_attn_matches_oracle(case):
     gb = bits(g)
     r = oracle_attn(q, kk, v, idx, tau, shared)
     err = np.abs(bf16_to_f64(gb) - bf16_to_f64(r))
-    log(f"  max abs err {err.max():.3e}")
+    rel = attn_row_rel(gb, r)
+    log(f"  max abs err {err.max():.3e}; row-relative err max {rel.max():.3e} "
+        f"(bound {ATTN_ROW_REL}; a dropped 32-index tile moves a row by ~0.1)")
     assert np.isfinite(bf16_to_f64(gb)).all()
     assert err.max() <= ATTN_ATOL
+    assert rel.max() <= ATTN_ROW_REL
 
 
 def test_attn_single_index_is_exact_row():

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import ATTN_ATOL, bf16_to_f64, check_index_sets, check_scores, log
+from helpers import ATTN_ATOL, ATTN_ROW_REL, attn_row_rel, bf16_to_f64, check_index_sets, check_scores, log
 from long_context_sparse_idx_amd import inputs, lcsi
 from long_context_sparse_idx_amd.runner import Workload
 
@@ -94,6 +94,7 @@ def check_workload(name, n_slots=None, batches=(0,), allf_overlap=False):
     pos = sample_positions(wl)
     rows_t = torch.tensor([p - wl.q_pos0 for p in pos], device="cuda")
     swaps = 0
+    worst_rel = 0.0
     for b in batches:
         for fi, layer in enumerate(run.pattern_f):
             x = run.idx_in[layer]
@@ -119,8 +120,12 @@ def check_workload(name, n_slots=None, batches=(0,), allf_overlap=False):
                 o = gathered_attn_oracle(run, l, b, pos, g_idx)
                 g = u16(run.outs[l][b].index_select(0, rows_t))
                 err = float(np.abs(bf16_to_f64(g) - bf16_to_f64(o)).max())
+                rel = float(attn_row_rel(g, o).max())
+                worst_rel = max(worst_rel, rel)
                 assert err <= ATTN_ATOL, f"{name} b={b} layer {l}: max abs err {err}"
-        log(f"  b={b}: {len(pos)} rows x {nf} F layers checked, near-tie swaps {swaps}")
+                assert rel <= ATTN_ROW_REL, f"{name} b={b} layer {l}: row-relative err {rel}"
+        log(f"  b={b}: {len(pos)} rows x {nf} F layers checked, near-tie swaps {swaps}, "
+            f"attention row-relative err max {worst_rel:.3e} (bound {ATTN_ROW_REL})")
     return run
 
 

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import ATTN_ATOL, bf16_to_f64, bits, check_index_sets, log
+from helpers import ATTN_ATOL, ATTN_ROW_REL, attn_row_rel, bf16_to_f64, bits, check_index_sets, log
 from long_context_sparse_idx_amd import inputs, lcsi
 
 pytestmark = pytest.mark.gpu
@@ -150,6 +150,21 @@ def test_decode_patterns(name, n_slots):
     outs, cache, _ = run_group(wl, wl.pattern, f_dev, a_dev, n_slots=n_slots)
     pos = np.array([wl.q_pos0], np.int64)
     f_pos = [l for l, f in enumerate(wl.pattern) if f]
+    # With one slot the cache ends up holding only the last F layer's set;
+    # the sets the earlier groups used are recomputed by the same call on the
+    # same inputs (results are deterministic), so every layer is checked.
+    sets = []
+    for fi, x in enumerate(f_dev):
+        if n_slots > 1 or fi == len(f_pos) - 1:
+            sets.append(cache[fi % n_slots].cpu().numpy())
+            continue
+        d = lcsi.indexer_desc(x["q"], x["k"], x["w"], wl.top_k, wl.q_pos0, k_scale=x["k_scale"])
+        ws = torch.empty(lcsi.idx_score_topk_ws_bytes(d) // 4 + 64, device="cuda")
+        idx = torch.empty((wl.B, 1, wl.top_k), dtype=torch.int32, device="cuda")
+        lcsi.idx_score_topk(d, idx, ws)
+        torch.cuda.synchronize()
+        sets.append(idx.cpu().numpy())
+    worst = 0.0
     for b in range(wl.B):
         cur = None
         fi = 0
@@ -159,17 +174,19 @@ def test_decode_patterns(name, n_slots):
                 keys = x["k"][b].numpy() if wl.key_fp8 else bits(x["k"][b])
                 rS, ridx = oracle.score_select(bits(x["q"][b]), x["w"][b].numpy(), keys, pos, wl.top_k,
                                                k_scale=x["k_scale"][b].numpy() if wl.key_fp8 else None)
-                slot = fi % n_slots
-                cur = cache[slot, b].cpu().numpy()
-                if n_slots > 1 or fi == len(f_pos) - 1:
-                    check_index_sets(cur[0], ridx[0], rS[0, :wl.q_pos0 + 1], wl.top_k, f"b={b} l={l}")
+                cur = sets[fi][b]
+                check_index_sets(cur[0], ridx[0], rS[0, :wl.q_pos0 + 1], wl.top_k, f"b={b} l={l}")
                 fi += 1
             y = a_in[l]
             K = bits(y["k"][b])
             o = oracle.attn(bits(y["q"][b]), K, (K, wl.D_v), cur, inputs.sm_scale(wl))
-            if n_slots > 1 or l >= f_pos[-1]:
-                err = np.abs(bf16_to_f64(bits(outs[l][b])) - bf16_to_f64(o)).max()
-                assert err <= ATTN_ATOL, (b, l, err)
+            g = bits(outs[l][b])
+            err = np.abs(bf16_to_f64(g) - bf16_to_f64(o)).max()
+            rel = float(attn_row_rel(g, o).max())
+            worst = max(worst, rel)
+            assert err <= ATTN_ATOL, (b, l, err)
+            assert rel <= ATTN_ROW_REL, (b, l, rel)
+    log(f"  every layer checked; row-relative attention error max {worst:.3e} (bound {ATTN_ROW_REL})")
 
 
 def test_leading_s_layer_is_rejected():
