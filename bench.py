@@ -58,7 +58,7 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_entry(workload: str, kernel_prefix: str):
+def counter_entry(workload: str, kernel_prefix: str, kernel_suffix: str = ""):
     """The committed FETCH_SIZE / WRITE_SIZE entry of a kernel (HBM bytes per
     launch), or None when there is none for this workload or a source it was
     taken from has changed since."""
@@ -68,7 +68,8 @@ def counter_entry(workload: str, kernel_prefix: str):
     except OSError:
         return None
     for e in doc.get("entries", []):
-        if e["workload"] != workload or not e["kernel"].startswith(kernel_prefix):
+        if (e["workload"] != workload or not e["kernel"].startswith(kernel_prefix)
+                or not e["kernel"].endswith(kernel_suffix)):
             continue
         if all(source_sha(s) == h for s, h in e["sources"].items()):
             return e
@@ -381,7 +382,9 @@ def main():
     fused = n_fused > 0
     peak = PEAK_FP8_TFLOPS if wl.q_fp8 else PEAK_BF16_TFLOPS
     score_launch_ms = float(np.mean(score_ms)) / (nchunk * n_f)
-    score_counters = counter_entry(wl.name, "score_prefill_kernel" if wl.T_q > 1 else "score_splitkey_kernel")
+    # (the dominant variant: the fused candidate pass where a chunk plans it)
+    score_counters = (counter_entry(wl.name, "score_prefill_kernel", ", true>" if fused else ", false>")
+                      if wl.T_q > 1 else counter_entry(wl.name, "score_splitkey_kernel"))
     if wl.T_q > 1:
         achieved = pairs * flops_per_pair * n_f / score_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -416,12 +419,30 @@ def main():
         return {"kernel": entry["kernel"], "bytes_per_launch": entry["bytes_per_launch"],
                 "launch_ms_this_run": round(launch_ms, 4), "GBps": round(gbs, 1),
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+    def hbm_stage(primary, others, stage_ms):
+        """A stage of several kernels (select chain, attention + merge): its
+        bytes per call = the counted bytes of all its kernels over the calls
+        of its first kernel, against the stage's time per call here."""
+        e0 = counter_entry(wl.name, primary)
+        if e0 is None:
+            return None
+        parts = [e0] + [e for e in (counter_entry(wl.name, o) for o in others) if e is not None]
+        total = sum(e["bytes_per_launch"] * e["dispatches"] for e in parts) / e0["dispatches"]
+        gbs = total / (stage_ms / 1e3) / 1e9
+        return {"kernels": [e["kernel"] for e in parts], "bytes_per_call": int(total),
+                "call_ms_this_run": round(stage_ms, 4), "GBps": round(gbs, 1),
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    select_ms_call = float(np.mean(select_ms)) / (nchunk * n_f)
     hbm_block = {
-        "source": "bytes per launch from profiles/hbm_counters.json (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE, "
-                  "copy- and read-calibrated, same kernel sources); launch times measured in this run",
+        "source": "bytes per launch from profiles/hbm_counters.json (rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                  "runs of the same kernel sources, scaled by a 1 GiB copy counted in the same runs); "
+                  "launch times measured in this run",
         "score": hbm(score_counters, score_launch_ms),
-        "select": hbm(counter_entry(wl.name, "select_"), float(np.mean(select_ms)) / (nchunk * n_f)),
-        "attention": hbm(counter_entry(wl.name, "attn_kernel"), float(np.mean(attn_ms)) / (nchunk * L)),
+        "select": (hbm_stage("select_kernel", (), select_ms_call) if wl.T_q > 1 else
+                   hbm_stage("select_thresh_kernel", ("select_filter_kernel", "select_final_kernel"),
+                             select_ms_call)),
+        "attention": hbm_stage("attn_kernel", ("attn_merge_kernel",), float(np.mean(attn_ms)) / (nchunk * L)),
     }
 
     extra = {}

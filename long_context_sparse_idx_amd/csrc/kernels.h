@@ -68,7 +68,6 @@ struct SelectArgs {
     // few long rows (set by launch_select from the workspace past the scores)
     int nseg;                 // segments per row
     int64_t seg_len;          // scores per segment
-    uint32_t *tau;            // [rows] sampled threshold key
     int32_t *cnt;             // [rows][nseg] candidates per segment (-1: overflow)
     uint32_t *ckey;           // [rows][nseg][cap] candidate keys
     int32_t *cidx;            // [rows][nseg][cap] candidate positions

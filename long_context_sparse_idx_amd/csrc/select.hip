@@ -18,21 +18,22 @@
 // instead):
 //  A  n <= 16384: the whole row's keys sit in LDS; select there.
 //  B  longer rows: 8192 sampled scores (32 evenly spaced runs of 256) give
-//     a threshold tau expected to pass ~2.5k entries; one streaming pass
-//     keeps every entry with key >= tau in per-wave ordered LDS lists, and
-//     the exact select runs on those.  If fewer than k entries pass, or a
-//     list overflows, the row falls back to C.  The result never depends on
-//     the sample, only the cost does.
+//     a threshold tau that somewhat more than k entries are expected to
+//     reach (four standard deviations of the sampling error above k); one
+//     streaming pass keeps every entry with key >= tau in per-wave ordered
+//     LDS lists, and the exact select runs on those.  If fewer than k
+//     entries pass, or a list overflows, the row falls back to C.  The
+//     result never depends on the sample, only the cost does.
 //  C  exact radix select and compaction streaming the row from memory.
 //
 // Few long rows (decode: a handful of sequences, each with up to a million
 // scores) would leave most of the chip idle with one workgroup per row, so
-// they take a three-kernel form of path B: one workgroup per row finds the
-// sampled threshold; many workgroups per row filter one segment each into
-// a per-segment candidate list in the workspace (ordered); one workgroup
-// per row gathers the lists (ascending positions, segment after segment)
-// and runs the exact select on them -- or path C when a segment overflowed
-// or fewer than k entries passed.
+// they take a two-kernel form of path B: many workgroups per row each find
+// the row's sampled threshold (the same in all of them) and filter one
+// segment into a per-segment candidate list in the workspace (ordered); one
+// workgroup per row gathers the lists (ascending positions, segment after
+// segment) and runs the exact select on them -- or path C when a segment
+// overflowed or fewer than k entries passed.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -52,23 +53,91 @@ constexpr int NSUB = 4;           // histogram copies (waves w and w+4k share on
 struct Shared {
     union {
         uint32_t keys[NLDS];                     // path A
-        uint32_t samp[NSAMP];                    // path B, before filtering
         struct {
             uint32_t key[NW * CAPW];
             int32_t idx[NW * CAPW];
         } cand;                                  // path B candidates
     } u;
-    uint32_t hist[NSUB][256];
+    uint32_t hist[3][NSUB][256] __attribute__((aligned(16)));  // radix histograms, three in rotation
     int wcnt[NW];
     int wgt[NW];
     int wtie[NW];
-    uint32_t kth;
-    int rem;
-    int ge;
-    int full;  // the bin holding the rank-th key is taken whole
+    int nsmall;
+    uint32_t small[64];           // the keys of a small final bin (offsets)
     uint32_t wmin[NW], wmax[NW];  // per-wave key range, written while filling LDS
-    uint32_t kmin, kmax;
 };
+
+// ---- wave-wide sums, scans and ranges through DPP lane moves and
+// v_readlane (no LDS traffic).  Rows are the four 16-lane quarters of a
+// wave; a DPP source lane outside the row reads as 0.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_SHL = 0x100;   // + n: lane i takes lane i + n of its row
+constexpr int DPP_ROW_SHR = 0x110;   // + n: lane i takes lane i - n of its row
+constexpr int DPP_ROW_ROR = 0x120;   // + n: rotate within the row
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+    v += dpp<DPP_QUAD_XOR1>(v);
+    v += dpp<DPP_QUAD_XOR2>(v);
+    v += dpp<DPP_ROW_ROR + 4>(v);
+    v += dpp<DPP_ROW_ROR + 8>(v);  // every lane: its row's sum
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v)
+{
+    v = min(v, (uint32_t)dpp<DPP_QUAD_XOR1>((int)v));
+    v = min(v, (uint32_t)dpp<DPP_QUAD_XOR2>((int)v));
+    v = min(v, (uint32_t)dpp<DPP_ROW_ROR + 4>((int)v));
+    v = min(v, (uint32_t)dpp<DPP_ROW_ROR + 8>((int)v));
+    const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return min(a, b);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+    v = max(v, (uint32_t)dpp<DPP_QUAD_XOR1>((int)v));
+    v = max(v, (uint32_t)dpp<DPP_QUAD_XOR2>((int)v));
+    v = max(v, (uint32_t)dpp<DPP_ROW_ROR + 4>((int)v));
+    v = max(v, (uint32_t)dpp<DPP_ROW_ROR + 8>((int)v));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Inclusive suffix sum over lanes >= this one.
+__device__ __forceinline__ int wave_suffix_sum(int v)
+{
+    v += dpp<DPP_ROW_SHL + 1>(v);
+    v += dpp<DPP_ROW_SHL + 2>(v);
+    v += dpp<DPP_ROW_SHL + 4>(v);
+    v += dpp<DPP_ROW_SHL + 8>(v);  // suffix within the row; lane 16 r: row r's sum
+    const int r1 = __builtin_amdgcn_readlane(v, 16), r2 = __builtin_amdgcn_readlane(v, 32),
+              r3 = __builtin_amdgcn_readlane(v, 48);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row < 1 ? r1 : 0) + (row < 2 ? r2 : 0) + (row < 3 ? r3 : 0);
+}
+
+// Inclusive prefix sum over lanes <= this one.
+__device__ __forceinline__ int wave_prefix_sum(int v)
+{
+    v += dpp<DPP_ROW_SHR + 1>(v);
+    v += dpp<DPP_ROW_SHR + 2>(v);
+    v += dpp<DPP_ROW_SHR + 4>(v);
+    v += dpp<DPP_ROW_SHR + 8>(v);  // prefix within the row; lane 16 r + 15: row r's sum
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
 
 // ---- element visitors: each thread calls f(key) for its share ------------
 
@@ -78,6 +147,20 @@ struct LdsKeys {
     template <class F> __device__ void visit(F f) const
     {
         for (int i = threadIdx.x; i < n; i += NT) f(keys[i]);
+    }
+};
+
+// Keys held in registers: IT keys per thread, key u valid where bit u of
+// `valid` is set.
+template <int IT>
+struct RegKeys {
+    uint32_t k[IT];
+    uint32_t valid;
+    template <class F> __device__ __forceinline__ void visit(F f) const
+    {
+#pragma unroll
+        for (int u = 0; u < IT; ++u)
+            if ((valid >> u) & 1u) f(k[u]);
     }
 };
 
@@ -118,137 +201,130 @@ struct GlobalPairs {
 };
 
 // Find the rank-th largest key (rank >= 1, at most the number of visited
-// keys).  On return sh.kth is that key and sh.rem the number of entries
-// equal to it that belong to the top `rank`.
+// keys).  Returns that key and the number of entries equal to it that
+// belong to the top `rank` -- the same in every thread.
 //
-// A first pass finds the smallest and largest key; the 8-bit digit passes
-// then run on the offset key - kmin, starting at the highest bit of the
-// range kmax - kmin, so the first 256 bins span the keys actually present
-// (scores of one row share sign and exponent bits, and a digit over those
-// bits would put nearly every key into one or two bins).
+// The 8-bit digit passes run on the offset key - kmin (kmin, kmax: the
+// smallest and largest key), starting at the highest bit of the range
+// kmax - kmin, so the first 256 bins span the keys actually present (scores
+// of one row share sign and exponent bits, and a digit over those bits
+// would put nearly every key into one or two bins).  A pass is one
+// histogram (LDS atomics into one of NSUB copies by wave), one barrier, and
+// the bin search, which every wave does for itself on the shared counts.
+// The histograms rotate over three buffers: the one a pass fills was last
+// read two passes earlier, and the pass before clears it during its visit.
+// When at most 64 keys are left in the chosen bin they are collected and
+// ranked directly instead of further passes.
 // resolve < 32 stops once that many offset bits from the top are fixed and
-// at most max_ge keys lie at or above the current bin: sh.kth is then kmin +
-// the offset prefix with the lower bits cleared -- a lower bound of the
-// rank-th key that at least `rank` and at most max_ge keys reach (used for
-// the sampled threshold, where only a bound is needed; max_ge keeps the
-// bound tight when the keys span a wide range, e.g. scores of both signs).
+// at most max_ge keys lie at or above the current bin: the key returned is
+// then kmin + the offset prefix with the lower bits cleared -- a lower
+// bound of the rank-th key that at least `rank` and at most max_ge keys
+// reach (used for sampled thresholds, where only a bound is needed).
+// ranged = true: the caller has written every wave's key range with
+// wave_range and called radix_prepare, both before a barrier.  Two calls
+// must be separated by a barrier (the second clears what the first reads).
+struct Kth {
+    uint32_t key;
+    int rem;
+};
+
 // The smallest and largest of a thread's keys (kmn, kmx) reduced over the
 // wave into its slot of sh.wmin / sh.wmax (every wave writes its slot; a
-// wave without keys writes the empty range).  Callers that fill LDS do this
-// before the barrier that ends the fill, so radix_find(..., ranged = true)
-// needs no pass of its own over the keys for their range.
+// wave without keys writes the empty range).
 __device__ __forceinline__ void wave_range(Shared &sh, uint32_t kmn, uint32_t kmx)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        kmn = min(kmn, (uint32_t)__shfl_xor(kmn, o));
-        kmx = max(kmx, (uint32_t)__shfl_xor(kmx, o));
-    }
+    kmn = wave_min(kmn);
+    kmx = wave_max(kmx);
     if ((threadIdx.x & 63) == 0) {
         sh.wmin[threadIdx.x >> 6] = kmn;
         sh.wmax[threadIdx.x >> 6] = kmx;
     }
 }
 
+// Clears the first pass's histograms and the small-bin count.
+__device__ __forceinline__ void radix_prepare(Shared &sh)
+{
+    for (int i = threadIdx.x; i < NSUB * 256; i += NT) (&sh.hist[0][0][0])[i] = 0;
+    if (threadIdx.x == 0) sh.nsmall = 0;
+}
+
 template <class Src>
-__device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 32, int max_ge = 0x7FFFFFFF,
-                           bool ranged = false)
+__device__ Kth radix_find(Shared &sh, const Src &src, int rank, int resolve = 32, int max_ge = 0x7FFFFFFF,
+                          bool ranged = false)
 {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    uint32_t kmin_all = 0xFFFFFFFFu, kmax_all = 0u;
-    if (ranged) {
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-            kmin_all = min(kmin_all, sh.wmin[v]);
-            kmax_all = max(kmax_all, sh.wmax[v]);
-        }
-    } else {
-        if (tid == 0) {
-            sh.kmin = 0xFFFFFFFFu;
-            sh.kmax = 0u;
-        }
-        __syncthreads();
+    if (!ranged) {
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
         src.visit([&](uint32_t key) {
             kmn = min(kmn, key);
             kmx = max(kmx, key);
         });
+        wave_range(sh, kmn, kmx);
+        radix_prepare(sh);
+        __syncthreads();
+    }
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            kmn = min(kmn, (uint32_t)__shfl_xor(kmn, o));
-            kmx = max(kmx, (uint32_t)__shfl_xor(kmx, o));
-        }
-        if (lane == 0) {
-            atomicMin(&sh.kmin, kmn);
-            atomicMax(&sh.kmax, kmx);
-        }
-        __syncthreads();
-        kmin_all = sh.kmin;
-        kmax_all = sh.kmax;
+    for (int v = 0; v < NW; ++v) {
+        kmin = min(kmin, sh.wmin[v]);
+        kmax = max(kmax, sh.wmax[v]);
     }
-    const uint32_t kmin = kmin_all, range = kmax_all - kmin;
-    if (range == 0) {  // all keys equal: the rank-th is that key
-        if (tid == 0) {
-            sh.kth = kmin;
-            sh.rem = rank;
-        }
-        __syncthreads();
-        return;
-    }
+    const uint32_t range = kmax - kmin;
+    if (range == 0) return {kmin, rank};  // all keys equal: the rank-th is that key
     const int msb = 31 - __builtin_clz(range);
     uint32_t mask = msb == 31 ? 0u : ~((2u << msb) - 1u);  // offset bits already fixed (all zero)
     uint32_t prefix = 0;                                    // fixed offset bits
     int rem = rank;
     int hi = msb;  // highest bit of the next digit
 #pragma unroll 1
-    while (true) {
+    for (int p = 0;; ++p) {
         const int shift = hi >= 7 ? hi - 7 : 0;
         const uint32_t dmask = (2u << (hi - shift)) - 1u;  // digit width hi-shift+1 <= 8 bits
-        for (int i = tid; i < NSUB * 256; i += NT) (&sh.hist[0][0])[i] = 0;
-        __syncthreads();
-        uint32_t *hw = sh.hist[w % NSUB];
+        const int b = p % 3;
+        uint32_t *hw = sh.hist[b][w % NSUB];
+        for (int i = tid; i < NSUB * 256; i += NT) (&sh.hist[(p + 1) % 3][0][0])[i] = 0;
         src.visit([&](uint32_t key) {
             const uint32_t off = key - kmin;
             if ((off & mask) == prefix) atomicAdd(&hw[(off >> shift) & dmask], 1u);
         });
         __syncthreads();
-        if (tid < 64) {
-            uint32_t c[4];
+        // bin search (every wave): lane l owns bins 4l .. 4l+3
+        uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t v = 0;
-#pragma unroll
-                for (int h = 0; h < NSUB; ++h) v += sh.hist[h][4 * lane + e];
-                c[e] = v;
-            }
-            const int tot = (int)(c[0] + c[1] + c[2] + c[3]);
-            int suf = tot;  // inclusive suffix sum over lanes >= this one
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int t = __shfl_down(suf, o);
-                if (lane + o < 64) suf += t;
-            }
-            const int above = suf - tot;
-            if (above < rem && rem <= suf) {
-                int acc = above;
-                for (int e = 3; e >= 0; --e) {
-                    if (acc + (int)c[e] >= rem) {
-                        sh.kth = prefix | ((uint32_t)(4 * lane + e) << shift);
-                        sh.rem = rem - acc;
-                        sh.ge = (rank - rem) + acc + (int)c[e];  // keys at or above this bin
-                        sh.full = (int)c[e] == rem - acc;
-                        break;
-                    }
-                    acc += (int)c[e];
+        for (int h = 0; h < NSUB; ++h) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(&sh.hist[b][h][4 * lane]);
+            c[0] += v.x;
+            c[1] += v.y;
+            c[2] += v.z;
+            c[3] += v.w;
+        }
+        const int tot = (int)(c[0] + c[1] + c[2] + c[3]);
+        const int suf = wave_suffix_sum(tot);  // over lanes >= this one
+        const int above = suf - tot;
+        const bool found = above < rem && rem <= suf;  // exactly one lane
+        uint32_t f_prefix = 0;
+        int f_rem = 0, f_ge = 0, f_c = 0;
+        if (found) {
+            int acc = above;
+            for (int e = 3; e >= 0; --e) {
+                if (acc + (int)c[e] >= rem) {
+                    f_prefix = prefix | ((uint32_t)(4 * lane + e) << shift);
+                    f_rem = rem - acc;
+                    f_ge = (rank - rem) + acc + (int)c[e];  // keys at or above this bin
+                    f_c = (int)c[e];
+                    break;
                 }
+                acc += (int)c[e];
             }
         }
-        __syncthreads();
-        prefix = sh.kth;
-        rem = sh.rem;
+        const int fl = __ffsll((long long)ballot(found)) - 1;
+        prefix = __builtin_amdgcn_readlane(f_prefix, fl);
+        rem = __builtin_amdgcn_readlane(f_rem, fl);
+        const int ge = __builtin_amdgcn_readlane(f_ge, fl);
+        const int binc = __builtin_amdgcn_readlane(f_c, fl);
         mask |= dmask << shift;
-        if (shift == 0 || (msb - shift + 1 >= resolve && sh.ge <= max_ge)) break;
-        if (resolve == 32 && sh.full && prefix != 0) {
+        if (shift == 0 || (msb - shift + 1 >= resolve && ge <= max_ge)) break;
+        if (resolve == 32 && binc == rem && prefix != 0) {
             // every key of the bin is taken: the keys above offset prefix - 1
             // (this bin and everything above it) are exactly the top `rank`,
             // so the threshold is prefix - 1 with no ties to count
@@ -256,25 +332,42 @@ __device__ void radix_find(Shared &sh, const Src &src, int rank, int resolve = 3
             rem = 0;
             break;
         }
+        if (resolve == 32 && binc <= 64) {
+            // at most 64 keys left in the bin: collect them and rank them
+            // directly -- the rem-th largest x has fewer than rem keys above
+            // it and at least rem at or above it
+            const uint32_t bmask = mask, bprefix = prefix;
+            src.visit([&](uint32_t key) {
+                const uint32_t off = key - kmin;
+                if ((off & bmask) == bprefix) sh.small[atomicAdd(&sh.nsmall, 1)] = off;
+            });
+            __syncthreads();
+            const uint32_t x = lane < binc ? sh.small[lane] : 0u;
+            int gt = 0, geq = 0;
+            for (int j = 0; j < binc; ++j) {  // (uniform; lane j's key read into a scalar)
+                const uint32_t y = __builtin_amdgcn_readlane(x, j);
+                gt += y > x;
+                geq += y >= x;
+            }
+            const int f2 = __ffsll((long long)ballot(lane < binc && gt < rem && rem <= geq)) - 1;
+            prefix = __builtin_amdgcn_readlane(x, f2);
+            rem -= __builtin_amdgcn_readlane(gt, f2);
+            break;
+        }
         hi = shift - 1;
     }
-    __syncthreads();  // every thread has read sh.kth / sh.rem above
-    if (tid == 0) {
-        sh.kth = kmin + prefix;
-        sh.rem = rem;
-    }
-    __syncthreads();
+    return {kmin + prefix, rem};
 }
 
 // Ordered compaction over per-wave segments visited in ascending position
 // order.  Seg::get(w, j, key, pos) returns false past the end of segment w;
 // Seg::len(w) is an upper bound on its length (a multiple of 64 not needed).
 template <class Seg>
-__device__ void emit(Shared &sh, const Seg &seg, int32_t *out, int k)
+__device__ void emit(Shared &sh, const Seg &seg, int32_t *out, int k, Kth t)
 {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const uint32_t kth = sh.kth;
-    const int need = sh.rem;
+    const uint32_t kth = t.key;
+    const int need = t.rem;
     const int len = seg.len(w);
     int gt = 0, tie = 0;
     for (int j = lane; j < len; j += 64) {
@@ -285,8 +378,8 @@ __device__ void emit(Shared &sh, const Seg &seg, int32_t *out, int k)
             tie += key == kth;
         }
     }
-    gt = wave_sum_int(gt);
-    tie = wave_sum_int(tie);
+    gt = wave_sum(gt);
+    tie = wave_sum(tie);
     if (lane == 0) {
         sh.wgt[w] = gt;
         sh.wtie[w] = tie;
@@ -308,6 +401,50 @@ __device__ void emit(Shared &sh, const Seg &seg, int32_t *out, int k)
         const uint64_t bs = ballot(sel);
         const int slot = out_off + lanes_below(bs);
         if (sel && slot < k) out[slot] = pos;
+        tie_off += __popcll(bt);
+        out_off += __popcll(bs);
+    }
+}
+
+// The same compaction for keys held in registers: thread (w, lane) holds
+// entries lane + 64 u (u = 0 .. IT-1) of wave w's run, the waves' runs
+// follow one another, and every run is in ascending position order.
+template <int IT>
+__device__ void emit_regs(Shared &sh, const RegKeys<IT> &rk, const int32_t (&pos)[IT], int32_t *out, int k, Kth t)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t kth = t.key;
+    const int need = t.rem;
+    int gt = 0, tie = 0;
+#pragma unroll
+    for (int u = 0; u < IT; ++u)
+        if ((rk.valid >> u) & 1u) {
+            gt += rk.k[u] > kth;
+            tie += rk.k[u] == kth;
+        }
+    gt = wave_sum(gt);
+    tie = wave_sum(tie);
+    if (lane == 0) {
+        sh.wgt[w] = gt;
+        sh.wtie[w] = tie;
+    }
+    __syncthreads();
+    int tie_off = 0, out_off = 0;
+    for (int v = 0; v < w; ++v) {
+        const int take = min(max(need - tie_off, 0), sh.wtie[v]);
+        out_off += sh.wgt[v] + take;
+        tie_off += sh.wtie[v];
+    }
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+        if (ballot((rk.valid >> u) != 0u) == 0) break;  // no lane has entries from slot u on
+        const bool ok = (rk.valid >> u) & 1u;
+        const bool is_tie = ok && rk.k[u] == kth;
+        const uint64_t bt = ballot(is_tie);
+        const bool sel = ok && (rk.k[u] > kth || (is_tie && tie_off + lanes_below(bt) < need));
+        const uint64_t bs = ballot(sel);
+        const int slot = out_off + lanes_below(bs);
+        if (sel && slot < k) out[slot] = pos[u];
         tie_off += __popcll(bt);
         out_off += __popcll(bs);
     }
@@ -420,9 +557,10 @@ __device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t
             }
         }
         wave_range(sh, kmn, kmx);
+        radix_prepare(sh);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.cand.key, c}, k, 32, 0x7FFFFFFF, true);
-        emit(sh, LdsPairSeg{&sh, c, seg}, out, k);
+        const Kth t = radix_find(sh, LdsKeys{sh.u.cand.key, c}, k, 32, 0x7FFFFFFF, true);
+        emit(sh, LdsPairSeg{&sh, c, seg}, out, k, t);
         return;
     }
     if (c == n && n <= NLDS) {
@@ -449,49 +587,85 @@ __device__ void select_from_pairs(Shared &sh, const uint32_t *cp, int c, int64_t
             }
         }
         wave_range(sh, kmn, kmx);
+        radix_prepare(sh);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.keys, c}, k, 32, 0x7FFFFFFF, true);
-        emit(sh, LdsSeg{&sh, c, seg}, out, k);
+        const Kth t = radix_find(sh, LdsKeys{sh.u.keys, c}, k, 32, 0x7FFFFFFF, true);
+        emit(sh, LdsSeg{&sh, c, seg}, out, k, t);
         return;
     }
-    radix_find(sh, GlobalPairs{cp, c}, k);
-    emit(sh, GlobalPairSeg{cp, c, seg}, out, k);
+    const Kth t = radix_find(sh, GlobalPairs{cp, c}, k);
+    emit(sh, GlobalPairSeg{cp, c, seg}, out, k, t);
 }
 
 // Threshold for the sampled pass over a row of n > NLDS scores: 8192 scores
-// in 32 evenly spaced runs of 256 give the key tau that about 2.5k entries
-// of the row are expected to reach.  Every thread returns tau.
-__device__ uint32_t sampled_threshold(Shared &sh, const float *row, int64_t n, int k)
+// in 32 evenly spaced runs of 256 give a key tau that somewhat more than k
+// entries of the row are expected to reach.  With m = k * 8192 / n samples
+// expected at or above the row's k-th largest score, tau is a lower bound of
+// the r-th largest sample, r - 4 sqrt(r) = m: the expected pass count r n /
+// 8192 then exceeds k by four standard deviations of its sampling error (the
+// count of samples above a level is near-binomial, variance about r), so
+// fewer than k entries pass only rarely (the caller then takes the exact
+// path; the result never depends on tau, only the cost does).
+//
+// sample_begin issues the loads (16 scores per thread, kept in registers);
+// sample_threshold finds tau with the radix select, resolved to at least
+// 1/256 of the key range and until at most a quarter more samples than r
+// reach it.  Every thread returns tau.
+constexpr int RPW = NSB / NW;  // sample runs per wave
+struct Samples {
+    f32x4 v[RPW];
+};
+
+__device__ __forceinline__ Samples sample_begin(const float *row, int64_t n)
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    constexpr int RPW = NSB / NW;  // runs per wave, all loads issued first
-    f32x4 v[RPW];
+    Samples sp;
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
         const int s = w * RPW + u;
         const int64_t start = ((n - SBL) * s / (NSB - 1)) & ~(int64_t)3;
-        v[u] = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
+        sp.v[u] = *reinterpret_cast<const f32x4 *>(row + start + 4 * lane);
     }
+    return sp;
+}
+
+__device__ uint32_t sample_threshold(Shared &sh, const Samples &sp, int64_t n, int k)
+{
+    constexpr int IT = 4 * RPW;
+    uint32_t key[IT];
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
-        uint32_t *d = sh.u.samp + (w * RPW + u) * SBL + 4 * lane;
-        d[0] = order_key(v[u].x);
-        d[1] = order_key(v[u].y);
-        d[2] = order_key(v[u].z);
-        d[3] = order_key(v[u].w);
+        key[4 * u] = order_key(sp.v[u].x);
+        key[4 * u + 1] = order_key(sp.v[u].y);
+        key[4 * u + 2] = order_key(sp.v[u].z);
+        key[4 * u + 3] = order_key(sp.v[u].w);
     }
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+        kmn = min(kmn, key[u]);
+        kmx = max(kmx, key[u]);
+    }
+    wave_range(sh, kmn, kmx);
+    radix_prepare(sh);
     __syncthreads();
-    int64_t r = (5 * (int64_t)k * NSAMP + 2 * n - 1) / (2 * n);
+    const float m = (float)k * (float)NSAMP / (float)n;
+    const float sr = 0.5f * (4.f + sqrtf(16.f + 4.f * m));
+    int r = (int)ceilf(sr * sr);
     r = r < 1 ? 1 : (r > NSAMP ? NSAMP : r);
-    // a lower bound of the r-th sampled key, resolved to 1/256 of the
-    // samples' key range, is precise enough for a threshold -- unless its
-    // bin holds so many samples that the expected pass count would crowd
-    // the candidate lists (7/8 of their capacity); then refine further
+    // at most a quarter more samples than r at or above tau, and never so
+    // many that the expected pass count would crowd the candidate lists
+    // (7/8 of their capacity)
     const int64_t cap = (int64_t)NW * CAPW * 7 / 8 * NSAMP / n;
-    radix_find(sh, LdsKeys{sh.u.samp, NSAMP}, (int)r, 8, (int)(cap > r ? cap : r));
-    const uint32_t tau = sh.kth;
-    __syncthreads();  // every thread has read tau before the lists overwrite the samples
-    return tau;
+    int64_t mg = r + r / 4 + 4;
+    mg = mg < cap ? mg : cap;
+    const int max_ge = (int)(mg > r ? mg : r);
+
+    RegKeys<IT> rk;
+    rk.valid = (1u << IT) - 1u;
+#pragma unroll
+    for (int u = 0; u < IT; ++u) rk.k[u] = key[u];
+    return radix_find(sh, rk, r, 8, max_ge, true).key;
 }
 
 // One streaming pass over row[lo, hi) (lo a multiple of 4): every entry with
@@ -499,25 +673,49 @@ __device__ uint32_t sampled_threshold(Shared &sh, const float *row, int64_t n, i
 // contiguous part, a multiple of 256 entries long), so the lists visited
 // wave by wave are in ascending position order.  sh.wcnt[w] is the count of
 // wave w's passing entries (more than CAPW means its list overflowed).
-__device__ void filter_to_lists(Shared &sh, const float *row, int64_t lo_row, int64_t hi_row, uint32_t tau)
+// filter_begin issues the loads of a wave's first 1024 scores (so that they
+// can be in flight while tau is found); filter_finish does the pass.
+constexpr int FU = 4;  // f32x4 loads per lane per step of the pass
+struct FilterPart {
+    int64_t lo, hi;  // this wave's part of the range
+    f32x4 v[FU];     // its first FU * 256 scores
+};
+
+__device__ __forceinline__ FilterPart filter_begin(const float *row, int64_t lo_row, int64_t hi_row)
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t seg = (hi_row - lo_row + NW * 256 - 1) / (NW * 256) * 256;
-    const int64_t lo = lo_row + (int64_t)w * seg;
-    const int64_t hi = min<int64_t>(hi_row, lo + seg);
+    FilterPart p;
+    p.lo = lo_row + (int64_t)w * seg;
+    p.hi = min<int64_t>(hi_row, p.lo + seg);
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+        const int64_t i = p.lo + u * 256 + 4 * lane;
+        p.v[u] = i < p.hi ? *reinterpret_cast<const f32x4 *>(row + i) : f32x4{0, 0, 0, 0};
+    }
+    return p;
+}
+
+__device__ void filter_finish(Shared &sh, const float *row, const FilterPart &p, uint32_t tau)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t lo = p.lo, hi = p.hi;
     int cnt = 0;
     uint32_t *ck = sh.u.cand.key + w * CAPW;
     int32_t *ci = sh.u.cand.idx + w * CAPW;
-    constexpr int U = 4;
-    for (int64_t base = lo; base < hi; base += U * 256) {
-        f32x4 v[U];
+    f32x4 v[FU];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + u * 256 + 4 * lane;
-            v[u] = i < hi ? *reinterpret_cast<const f32x4 *>(row + i) : f32x4{0, 0, 0, 0};
+    for (int u = 0; u < FU; ++u) v[u] = p.v[u];
+    for (int64_t base = lo; base < hi; base += FU * 256) {
+        if (base != lo) {
+#pragma unroll
+            for (int u = 0; u < FU; ++u) {
+                const int64_t i = base + u * 256 + 4 * lane;
+                v[u] = i < hi ? *reinterpret_cast<const f32x4 *>(row + i) : f32x4{0, 0, 0, 0};
+            }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < FU; ++u) {
             const int64_t i = base + u * 256 + 4 * lane;
             const uint32_t k0 = order_key(v[u].x), k1 = order_key(v[u].y);
             const uint32_t k2 = order_key(v[u].z), k3 = order_key(v[u].w);
@@ -526,16 +724,22 @@ __device__ void filter_to_lists(Shared &sh, const float *row, int64_t lo_row, in
             const int c = (int)f0 + (int)f1 + (int)f2 + (int)f3;
             if (ballot(c > 0) == 0) continue;
             const uint64_t b0 = ballot(c & 1), b1 = ballot(c & 2), b2 = ballot(c & 4);
-            int p = cnt + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
-            if (f0) { if (p < CAPW) { ck[p] = k0; ci[p] = (int32_t)i; } ++p; }
-            if (f1) { if (p < CAPW) { ck[p] = k1; ci[p] = (int32_t)(i + 1); } ++p; }
-            if (f2) { if (p < CAPW) { ck[p] = k2; ci[p] = (int32_t)(i + 2); } ++p; }
-            if (f3) { if (p < CAPW) { ck[p] = k3; ci[p] = (int32_t)(i + 3); } ++p; }
+            int q = cnt + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
+            if (f0) { if (q < CAPW) { ck[q] = k0; ci[q] = (int32_t)i; } ++q; }
+            if (f1) { if (q < CAPW) { ck[q] = k1; ci[q] = (int32_t)(i + 1); } ++q; }
+            if (f2) { if (q < CAPW) { ck[q] = k2; ci[q] = (int32_t)(i + 2); } ++q; }
+            if (f3) { if (q < CAPW) { ck[q] = k3; ci[q] = (int32_t)(i + 3); } ++q; }
             cnt += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
         }
     }
     if (lane == 0) sh.wcnt[w] = cnt;
     __syncthreads();
+}
+
+__device__ __forceinline__ void filter_to_lists(Shared &sh, const float *row, int64_t lo_row, int64_t hi_row,
+                                                uint32_t tau)
+{
+    filter_finish(sh, row, filter_begin(row, lo_row, hi_row), tau);
 }
 
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
@@ -590,17 +794,20 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
             put(i + 3, v[u].w);
         }
         wave_range(sh, kmn, kmx);
+        radix_prepare(sh);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.keys, (int)n}, k, 32, 0x7FFFFFFF, true);
+        const Kth t = radix_find(sh, LdsKeys{sh.u.keys, (int)n}, k, 32, 0x7FFFFFFF, true);
         const int seg = (int)(((n + NW - 1) / NW + 63) / 64 * 64);
-        emit(sh, LdsSeg{&sh, (int)n, seg}, out, k);
+        emit(sh, LdsSeg{&sh, (int)n, seg}, out, k, t);
         return;
     }
 
     // ---- path B: sampled threshold, one streaming pass, exact select on
     // the candidates
-    const uint32_t tau = sampled_threshold(sh, row, n, k);
-    filter_to_lists(sh, row, 0, n, tau);
+    const Samples sp = sample_begin(row, n);          // samples first,
+    const FilterPart part = filter_begin(row, 0, n);  // then the pass's first scores (in flight while tau is found)
+    const uint32_t tau = sample_threshold(sh, sp, n, k);
+    filter_finish(sh, row, part, tau);
     int total = 0;
     bool overflow = false;
     for (int v = 0; v < NW; ++v) {
@@ -608,36 +815,71 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
         overflow |= sh.wcnt[v] > CAPW;
     }
     if (!overflow && total >= k) {
-        radix_find(sh, Candidates{&sh}, k);
-        emit(sh, CandSeg{&sh}, out, k);
+        const Kth t = radix_find(sh, Candidates{&sh}, k);
+        emit(sh, CandSeg{&sh}, out, k, t);
         return;
     }
 
     // ---- path C: exact, streaming the row from memory
     __syncthreads();
-    radix_find(sh, GlobalRow{row, n}, k);
+    const Kth kc = radix_find(sh, GlobalRow{row, n}, k);
     const int64_t seg = ((n + NW - 1) / NW + 63) / 64 * 64;
-    emit(sh, GlobalSeg{row, n, seg}, out, k);
+    emit(sh, GlobalSeg{row, n, seg}, out, k, kc);
 }
 
+// The per-segment candidate lists of one row in the workspace, read in
+// place: entry i of their concatenation lies in the last segment s with
+// pre[s] <= i (pre: list offsets by segment in LDS, INT_MAX past the last
+// segment; at most 64 segments), at slot i - pre[s] of segment s's list.
+struct SegLists {
+    const uint32_t *key;  // the row's first segment list (cap slots per segment)
+    const int32_t *idx;
+    const int *pre;
+    int total, cap;
+    __device__ __forceinline__ int64_t src(int i) const
+    {
+        int s = 0, base = 0;
+#pragma unroll
+        for (int step = 32; step >= 1; step >>= 1) {
+            const int pv = pre[s + step];
+            const bool mv = pv <= i;
+            s += mv ? step : 0;
+            base = mv ? pv : base;
+        }
+        return (int64_t)s * cap + (i - base);
+    }
+    template <class F> __device__ void visit(F f) const
+    {
+        for (int i = threadIdx.x; i < total; i += NT) f(key[src(i)]);
+    }
+};
+
+struct SegListSeg {
+    SegLists l;
+    int seg;  // entries per wave run
+    __device__ int len(int w) const { return seg; }
+    __device__ bool get(int w, int j, uint32_t &key, int32_t &pos) const
+    {
+        const int i = w * seg + j;
+        if (j >= seg || i >= l.total) return false;
+        const int64_t e = l.src(i);
+        key = l.key[e];
+        pos = l.idx[e];
+        return true;
+    }
+};
+
 // ---------------------------------------------------------------------------
-// Few long rows: threshold / segment filter / final select.
+// Few long rows: segment filter / final select.
 // ---------------------------------------------------------------------------
 constexpr int SEG_CAP = 2048;     // candidate slots per segment in the workspace
 
 __device__ __forceinline__ int64_t row_id(const SelectArgs &a, int b, int t) { return (int64_t)b * a.T_q + t; }
 
-__global__ __launch_bounds__(NT) void select_thresh_kernel(SelectArgs a)
-{
-    __shared__ Shared sh;
-    const int t = blockIdx.x, b = blockIdx.y;
-    const int64_t n = a.q_pos0 + t + 1;
-    if (n <= a.top_k) return;
-    const float *row = a.S + row_id(a, b, t) * a.ld;
-    const uint32_t tau = sampled_threshold(sh, row, n, a.top_k);
-    if (threadIdx.x == 0) a.tau[row_id(a, b, t)] = tau;
-}
-
+// One workgroup per (row, segment): the row's sampled threshold (every
+// workgroup of a row finds the same tau from the same samples), then the
+// segment's entries at or above it, in position order, into the segment's
+// slots of the workspace.
 __global__ __launch_bounds__(NT) void select_filter_kernel(SelectArgs a)
 {
     __shared__ Shared sh;
@@ -653,7 +895,11 @@ __global__ __launch_bounds__(NT) void select_filter_kernel(SelectArgs a)
         if (tid == 0) *cnt = 0;
         return;
     }
-    filter_to_lists(sh, a.S + r * a.ld, lo, hi, a.tau[r]);
+    const float *row = a.S + r * a.ld;
+    const Samples sp = sample_begin(row, n);            // samples first,
+    const FilterPart part = filter_begin(row, lo, hi);  // then the segment's first scores (in flight while tau is found)
+    const uint32_t tau = sample_threshold(sh, sp, n, a.top_k);
+    filter_finish(sh, row, part, tau);
     int off = 0, total = 0;
     bool overflow = false;
     for (int v = 0; v < NW; ++v) {
@@ -674,11 +920,17 @@ __global__ __launch_bounds__(NT) void select_filter_kernel(SelectArgs a)
     if (tid == 0) *cnt = total;
 }
 
+// One workgroup per row: the segments' lists gathered into registers
+// (ascending positions, segment after segment) and the exact select on them;
+// the exact select on the lists in memory when they hold more than the
+// registers; the exact path from the row itself when a segment overflowed or
+// fewer than k entries passed.
 __global__ __launch_bounds__(NT) void select_final_kernel(SelectArgs a)
 {
     __shared__ Shared sh;
-    __shared__ int pre[65];
-    const int tid = threadIdx.x, w = tid >> 6;
+    __shared__ int pre[128];  // list offsets by segment; past the last segment: INT_MAX
+    __shared__ int ptotal;
+    const int tid = threadIdx.x;
     const int t = blockIdx.x, b = blockIdx.y;
     const int64_t n = a.q_pos0 + t + 1;
     const int k = a.top_k;
@@ -696,63 +948,81 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelectArgs a)
         // negative count (overflowed segment) marks the row bad (-1 total)
         const int c = tid < a.nseg ? a.cnt[r * a.nseg + tid] : 0;
         const int v = c < 0 ? 0 : c;
-        int inc = v;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int u = __shfl_up(inc, o);
-            if (tid >= o) inc += u;
-        }
-        if (tid < a.nseg) pre[tid] = inc - v;
+        const int inc = wave_prefix_sum(v);
+        pre[tid] = tid < a.nseg ? inc - v : 0x7FFFFFFF;
+        pre[64 + tid] = 0x7FFFFFFF;
         const bool bad = ballot(c < 0) != 0;
-        if (tid == a.nseg - 1) pre[a.nseg] = bad ? -1 : inc;
+        if (tid == 63) ptotal = bad ? -1 : inc;
     }
     __syncthreads();
-    const int total = pre[a.nseg];
+    const int total = ptotal;
     if (total >= k && total <= NW * CAPW) {
-        // the concatenated lists, contiguous in LDS (ascending positions);
-        // every load of a thread is issued before the first store
+        // the concatenated lists (ascending positions) cut into NW runs of
+        // `run` entries, one per wave, held in registers: thread (w, lane)
+        // takes entries w * run + lane + 64 u.  Entry i lies in the last
+        // segment s with pre[s] <= i: a branch-free binary search for every
+        // entry of a thread first, then all its loads.
         constexpr int IT = NW * CAPW / NT;
-        uint32_t kv[IT];
-        int32_t iv[IT];
+        const int w = tid >> 6, lane = tid & 63;
+        const int run = ((total + NW - 1) / NW + 63) / 64 * 64;
+        int sg[IT], sb[IT];
+        RegKeys<IT> rk;
+        int32_t pos[IT];
+        rk.valid = 0u;
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
-            const int i = tid + u * NT;
-            kv[u] = 0u;
-            iv[u] = 0;
-            if (i < total) {
-                // segment holding entry i: the last s with pre[s] <= i
-                // (binary search over the ascending prefix; pre[0] = 0)
-                int s = 0;
-                for (int step = 32; step >= 1; step >>= 1)
-                    if (s + step < a.nseg && pre[s + step] <= i) s += step;
-                const int64_t src = (r * a.nseg + s) * SEG_CAP + (i - pre[s]);
-                kv[u] = a.ckey[src];
-                iv[u] = a.cidx[src];
+            sg[u] = 0;
+            sb[u] = 0;
+            if (64 * u >= run) continue;  // (uniform)
+            const int i = w * run + lane + 64 * u;
+            if (i < total) rk.valid |= 1u << u;
+            int s = 0, base = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1) {
+                const int pv = pre[s + step];
+                const bool mv = pv <= i;
+                s += mv ? step : 0;
+                base = mv ? pv : base;
             }
+            sg[u] = s;
+            sb[u] = i - base;
         }
         uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
-            const int i = tid + u * NT;
-            if (i < total) {
-                sh.u.cand.key[i] = kv[u];
-                sh.u.cand.idx[i] = iv[u];
-                kmn = min(kmn, kv[u]);
-                kmx = max(kmx, kv[u]);
+            rk.k[u] = 0u;
+            pos[u] = -1;
+            if ((rk.valid >> u) & 1u) {
+                const int64_t src = (r * a.nseg + sg[u]) * SEG_CAP + sb[u];
+                rk.k[u] = a.ckey[src];
+                pos[u] = a.cidx[src];
             }
         }
+#pragma unroll
+        for (int u = 0; u < IT; ++u)
+            if ((rk.valid >> u) & 1u) {
+                kmn = min(kmn, rk.k[u]);
+                kmx = max(kmx, rk.k[u]);
+            }
         wave_range(sh, kmn, kmx);
+        radix_prepare(sh);
         __syncthreads();
-        radix_find(sh, LdsKeys{sh.u.cand.key, total}, k, 32, 0x7FFFFFFF, true);
-        const int seg = ((total + NW - 1) / NW + 63) / 64 * 64;
-        emit(sh, LdsPairSeg{&sh, total, seg}, out, k);
+        const Kth t = radix_find(sh, rk, k, 32, 0x7FFFFFFF, true);
+        emit_regs(sh, rk, pos, out, k, t);
+        return;
+    }
+    if (total >= k) {
+        // more candidates than the registers hold: the exact select on the
+        // lists where they lie
+        const SegLists l{a.ckey + r * a.nseg * SEG_CAP, a.cidx + r * a.nseg * SEG_CAP, pre, total, SEG_CAP};
+        const Kth kl = radix_find(sh, l, k);
+        emit(sh, SegListSeg{l, ((total + NW - 1) / NW + 63) / 64 * 64}, out, k, kl);
         return;
     }
     // path C: exact, streaming the row from memory
-    (void)w;
-    radix_find(sh, GlobalRow{row, n}, k);
+    const Kth kc = radix_find(sh, GlobalRow{row, n}, k);
     const int64_t seg = ((n + NW - 1) / NW + 63) / 64 * 64;
-    emit(sh, GlobalSeg{row, n, seg}, out, k);
+    emit(sh, GlobalSeg{row, n, seg}, out, k, kc);
 }
 
 struct MultiPlan {
@@ -782,7 +1052,7 @@ size_t select_ws_bytes(int B, int T_q, int64_t q_pos0)
     const MultiPlan p = multi_plan(B, T_q, q_pos0);
     if (!p.on) return 0;
     const size_t rows = (size_t)B * T_q;
-    return align256(rows * 4) + align256(rows * p.nseg * 4) + 2 * align256(rows * p.nseg * SEG_CAP * 4);
+    return align256(rows * p.nseg * 4) + 2 * align256(rows * p.nseg * SEG_CAP * 4);
 }
 
 hipError_t launch_select(const SelectArgs &a_in, void *extra, hipStream_t st)
@@ -797,14 +1067,11 @@ hipError_t launch_select(const SelectArgs &a_in, void *extra, hipStream_t st)
     uint8_t *ws = (uint8_t *)extra;
     a.nseg = p.nseg;
     a.seg_len = p.seg_len;
-    a.tau = (uint32_t *)ws;
-    ws += align256(rows * 4);
     a.cnt = (int32_t *)ws;
     ws += align256(rows * p.nseg * 4);
     a.ckey = (uint32_t *)ws;
     ws += align256(rows * p.nseg * SEG_CAP * 4);
     a.cidx = (int32_t *)ws;
-    hipLaunchKernelGGL(select_thresh_kernel, dim3(a.T_q, a.B), dim3(NT), 0, st, a);
     hipLaunchKernelGGL(select_filter_kernel, dim3(a.nseg, a.T_q, a.B), dim3(NT), 0, st, a);
     hipLaunchKernelGGL(select_final_kernel, dim3(a.T_q, a.B), dim3(NT), 0, st, a);
     return hipGetLastError();

@@ -2,7 +2,9 @@
 byte-identical to the oracle's selection: same positions, ascending, same
 -1 padding.  Rows cover every path of the kernel: n <= k, whole row in LDS,
 the sampled-threshold pass, and the exact streaming fallback (heavy ties,
-all-equal rows, +-0, monotone rows)."""
+all-equal rows, +-0, monotone rows); for few long rows also lists longer
+than usual (recent positions scoring higher) and more candidates than the
+final select holds in registers (a tied plateau)."""
 import zlib
 
 import numpy as np
@@ -57,11 +59,19 @@ def rows(rng, B, T_q, T_kv, kind):
         return np.tile(-np.arange(n, dtype=np.float32), (R, 1))
     if kind == "positive":  # indexer-like: positive, concentrated
         return (2.0 + 0.4 * rng.standard_normal((R, n))).astype(np.float32)
+    if kind == "recent":  # the last 6144 positions score higher: a few long candidate lists
+        x = rng.standard_normal((R, n)).astype(np.float32)
+        x[:, -6144:] += 1.0
+        return x
+    if kind == "plateau":  # 5 % of the entries tie at the top: more candidates than a select holds in registers
+        x = rng.standard_normal((R, n)).astype(np.float32)
+        x[rng.random((R, n)) < 0.05] = 10.0
+        return x
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("kind", ["normal", "positive", "ties", "equal", "signed_zero", "increasing",
-                                  "decreasing"])
+                                  "decreasing", "recent", "plateau"])
 @pytest.mark.parametrize("shape", [
     (2, 6, 40000, 39994, 2048),   # sampled-threshold path (and fallback for ties)
     (1, 6, 16384, 16378, 2048),   # whole row in LDS
