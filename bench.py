@@ -440,8 +440,7 @@ def main():
                   "launch times measured in this run",
         "score": hbm(score_counters, score_launch_ms),
         "select": (hbm_stage("select_kernel", (), select_ms_call) if wl.T_q > 1 else
-                   hbm_stage("select_thresh_kernel", ("select_filter_kernel", "select_final_kernel"),
-                             select_ms_call)),
+                   hbm_stage("select_filter_kernel", ("select_final_kernel",), select_ms_call)),
         "attention": hbm_stage("attn_kernel", ("attn_merge_kernel",), float(np.mean(attn_ms)) / (nchunk * L)),
     }
 
