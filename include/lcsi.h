@@ -198,11 +198,13 @@ int idx_score_topk(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb,
 /* Sparse attention of every query head over the rows listed in
  * idx[b*idx_sb + t*idx_st + j], j < a->top_k (the index set of this row,
  * as written by idx_score_topk).  Output to a->out in bf16.
- * ws / ws_bytes: fp32 workspace for the partial results of a decode call
+ * ws / ws_bytes: workspace for the partial results of a decode call
  * (T_q == 1 with top_k > 256: each row's list runs in ceil(top_k / 256)
  * parts of equal length, a multiple of 32 indices, on separate workgroups,
- * then a log-sum-exp merge); the requirement is B * parts * H_q * D_v * 4
- * bytes rounded up to 256, plus B * parts * H_q * 8 bytes.  For any other
+ * then a log-sum-exp merge): each part's output divided by its softmax sum
+ * in fp16, then its (max logit, sum) in fp32.  The requirement is
+ * B * parts * H_q * D_v * 2 bytes rounded up to 256, plus
+ * B * parts * H_q * 8 bytes.  For any other
  * call it is 0 and ws may be NULL with ws_bytes NULL (workspace rule
  * above). */
 int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,

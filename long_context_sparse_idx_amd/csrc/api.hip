@@ -131,8 +131,8 @@ size_t attn_ws_bytes(const lcsi_attn *a, AttnPlan *plan_out = nullptr)
     if (plan_out) *plan_out = pl;
     if (pl.splits == 1) return 0;
     const size_t rows = (size_t)a->B * a->T_q * pl.splits * a->H_q;
-    const size_t o = (rows * a->D_v * sizeof(float) + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;
-    return o + rows * 2 * sizeof(float);
+    const size_t o = (rows * a->D_v * sizeof(uint16_t) + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;  // fp16 O / l
+    return o + rows * 2 * sizeof(float);                                                       // fp32 (m, l)
 }
 
 // The workspace rule shared by all calls (see lcsi.h).  Returns 1 for query
@@ -294,8 +294,8 @@ int run_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx
     aa.split_len = pl.split_len;
     if (aa.splits > 1) {
         const size_t rows = (size_t)a->B * a->T_q * aa.splits * a->H_q;
-        const size_t o = (rows * a->D_v * sizeof(float) + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;
-        aa.part_o = ws;
+        const size_t o = (rows * a->D_v * sizeof(uint16_t) + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;
+        aa.part_o = (uint16_t *)ws;
         aa.part_ml = (float *)((char *)ws + o);
     }
     return launch_attn(aa, s) == hipSuccess ? LCSI_OK : LCSI_EHIP;

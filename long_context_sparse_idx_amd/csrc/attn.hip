@@ -320,10 +320,17 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
             *reinterpret_cast<u32x2 *>(op + dt * 16) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
     } else {
+        // the part's own normalised output O / l in fp16 (a convex
+        // combination of V rows, so within fp16's range; 11 significant
+        // bits, more than the bf16 result keeps), and (m, l) in fp32
         const int64_t row = ((int64_t)b * a.T_q + t) * a.splits + split;
-        float *po = a.part_o + (row * a.H + head) * DV + ds * DVW + 4 * g;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t *po = a.part_o + (row * a.H + head) * DV + ds * DVW + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + dt * 16) = oacc[dt];
+        for (int dt = 0; dt < NDT; ++dt) {
+            const f32x4 o = oacc[dt] * inv;
+            *reinterpret_cast<u32x2 *>(po + dt * 16) = u32x2{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
+        }
         if (ds == 0 && g == 0) {
             float *pm = a.part_ml + (row * a.H + head) * 2;
             pm[0] = m_run;
@@ -332,8 +339,9 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// Combine the per-split partial results of one (query row, head):
-// O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s,
+// Combine the per-split partial results of one (query row, head): with
+// each part's normalised output N_s = O_s / l_s,
+// O = sum_s w_s N_s / sum_s w_s,  w_s = l_s 2^(m_s - M),  M = max_s m_s,
 // summed over s in ascending order.  One workgroup per (head, row); thread i
 // owns output dims 4i .. 4i+3.  S = the split count, fixed at compile time so
 // that every partial of a thread is loaded before the first is used.
@@ -353,7 +361,8 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
         const f32x2 ml = *reinterpret_cast<const f32x2 *>(a.part_ml + r * 2);
         ms[s] = ml[0];
         ls[s] = ml[1];
-        os[s] = *reinterpret_cast<const f32x4 *>(a.part_o + r * a.DV + d);
+        const u32x2 hv = *reinterpret_cast<const u32x2 *>(a.part_o + r * a.DV + d);
+        os[s] = f32x4{f16_lo(hv.x), f16_hi(hv.x), f16_lo(hv.y), f16_hi(hv.y)};
     }
     float M = -__builtin_inff();
 #pragma unroll
@@ -364,9 +373,9 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             if (ms[s] == -__builtin_inff()) continue;
-            const float f = __builtin_amdgcn_exp2f(ms[s] - M);
-            L += ls[s] * f;
-            o += os[s] * f;
+            const float ws = ls[s] * __builtin_amdgcn_exp2f(ms[s] - M);
+            L += ws;
+            o += os[s] * ws;
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;

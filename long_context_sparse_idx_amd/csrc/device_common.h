@@ -47,6 +47,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Two fp32 -> two IEEE fp16 (lo in the low half), round to nearest even,
+// and back (exact).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(f16x2, v)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(f16x2, v)[1]; }
+
 // Four OCP E4M3 bytes (one dword) -> four bf16 values packed in two dwords
 // (byte i -> half i), with the hardware conversion at scale 1.  Every finite
 // E4M3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is exactly a bf16

@@ -94,7 +94,7 @@ struct AttnArgs {
     int splits;               // key splits per query row (1 = write bf16 directly)
     int split_len;            // index entries per split (multiple of 32)
     int hgroups;              // workgroups sharing one row's heads (each takes H / hgroups of them)
-    float *part_o;            // [B*T_q][splits][H][DV] (splits > 1)
+    uint16_t *part_o;         // [B*T_q][splits][H][DV] fp16, the part's O / l (splits > 1)
     float *part_ml;           // [B*T_q][splits][H][2]
 };
 

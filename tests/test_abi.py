@@ -128,7 +128,7 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
     """Checked on the host before anything is launched: a decode call whose
     partials exceed the static scratch returns LCSI_ESCRATCH; bad
     descriptors fail as for sparse_attn."""
-    big = good_attn(B=64, T_q=1, H_q=64, q_pos0=99, top_k=2048)   # 64 * 8 * 64 * 2 KB > 48 MiB
+    big = good_attn(B=128, T_q=1, H_q=64, q_pos0=99, top_k=2048)  # 128 * 8 * 64 * 1 KB > 48 MiB
     rc = lcsi.lib.sparse_attn_noalloc(ctypes.byref(big), ctypes.c_void_p(FAKE), 2048, 2048, None)
     assert rc == lcsi.LCSI_ESCRATCH
     assert "scratch" in lcsi.strerror(rc)
@@ -261,7 +261,7 @@ def test_attn_query_mode():
     for B in (1, 2, 32, 300):
         rc, n = call_attn(good_attn(B=B, T_q=1, q_pos0=99, top_k=2048))
         parts, H, Dv = 8, 32, 512
-        po = (B * parts * H * Dv * 4 + 255) // 256 * 256
+        po = (B * parts * H * Dv * 2 + 255) // 256 * 256
         assert rc == 0 and n == po + B * parts * H * 8, (B, n)
     rc, n = call_attn(good_attn(B=2, T_q=1, q_pos0=99, top_k=256))
     assert rc == 0 and n == 0           # one part: no partials
