@@ -176,8 +176,8 @@ def measured_ceilings():
     """Practical ceilings on this GPU, for context beside the datasheet peaks:
     a library bf16 GEMM (8192^3, entries N(0,1)/8 like the indexer inputs),
     the score kernel's MFMA stream alone (libceiling.so), a 4 GiB
-    device-to-device copy and a 4 GiB read-only reduction.  All run after the
-    timed region."""
+    device-to-device copy, a 4 GiB read-only reduction (torch) and a 4 GiB
+    plain streaming read (libceiling.so).  All run after the timed region."""
     g = torch.Generator(device="cuda").manual_seed(0)
     n = 8192
     a = (torch.randn(n, n, device="cuda", generator=g) / 8).to(torch.bfloat16)
@@ -215,11 +215,42 @@ def measured_ceilings():
     e1.record()
     torch.cuda.synchronize()
     read = src.numel() * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    stream_read = read_ceiling(src)
     del src, s
     torch.cuda.empty_cache()
     res.update({"copy_4GiB_GBps": round(copy, 1), "copy_frac_of_peak": round(copy / PEAK_HBM_GBS, 4),
-                "read_4GiB_sum_GBps": round(read, 1), "read_frac_of_peak": round(read / PEAK_HBM_GBS, 4)})
+                "read_4GiB_sum_GBps": round(read, 1), "read_frac_of_peak": round(read / PEAK_HBM_GBS, 4),
+                "read_4GiB_stream_GBps": round(stream_read, 1),
+                "read_stream_frac_of_peak": round(stream_read / PEAK_HBM_GBS, 4)})
     return res
+
+
+def read_ceiling(buf: torch.Tensor) -> float:
+    """A plain streaming read of `buf` (libceiling.so): GB/s."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_idx_amd", "libceiling.so"))
+    lib.lcsi_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lib.lcsi_ceiling_read.restype = ctypes.c_int
+    n_wg = 4096
+    out = torch.empty(n_wg * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    nbytes = buf.numel() * buf.element_size()
+
+    def launch():
+        rc = lib.lcsi_ceiling_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
+                                   ctypes.c_void_p(out.data_ptr()), n_wg, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"lcsi_ceiling_read: {rc}")
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
 
 
 def split_ms(events, nchunk, L):
@@ -285,6 +316,14 @@ def secondary(name: str, steps: int, warmup: int):
         "indexer_share_allF": round((sc_f + se_f) / (sc_f + se_f + at_f), 3),
         "indexer_share_pattern": round((sc + se) / (sc + se + at), 3),
     }
+    if wl.T_q == 1:
+        # decode scores are memory-bound: the key bytes (+ fp8 scales), queries
+        # and weights read and the score row written, per F layer, over the
+        # evented step's score time
+        key_b = wl.D_I * (1 if wl.key_fp8 else 2) + (4 if wl.key_fp8 else 0)
+        q_b = wl.D_I * (1 if wl.q_fp8 else 2) + (8 if wl.q_fp8 else 4)
+        nbytes = wl.B * (wl.T_kv * (key_b + 4) + wl.H_I * q_b) * sum(wl.pattern)
+        out["score_algorithmic_GBps_evented"] = round(nbytes / (sc / 1e3) / 1e9, 1)
     log(f"[bench] {name}: {ms:.3f} ms/step ({out[unit]:.0f} {unit}), all-F {ms_f:.3f} ms, "
         f"x{out['speedup_vs_allF']} ({time.time() - t0:.1f} s)")
     del path

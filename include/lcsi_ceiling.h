@@ -1,7 +1,8 @@
 /*
- * lcsi_ceiling.h -- measurement helper of the benchmark, in its own library
- * (libceiling.so), not a step of the method: the practical matrix-core
- * ceiling of the indexer score kernel on this GPU.
+ * lcsi_ceiling.h -- measurement helpers of the benchmark, in their own
+ * library (libceiling.so), not steps of the method: the practical
+ * matrix-core ceiling of the indexer score kernel on this GPU, and the
+ * practical rate of a plain streaming read from HBM.
  *
  * lcsi_ceiling_mfma launches n_wg workgroups of 8 waves (two per SIMD, as
  * the score kernel) that each issue `blocks` times the score kernel's block
@@ -32,6 +33,14 @@ extern "C" {
 
 size_t lcsi_ceiling_data_elems(void);
 int lcsi_ceiling_mfma(const uint16_t *data, float *out, int n_wg, int blocks, int mode, void *stream);
+
+/* lcsi_ceiling_read reads every 16-byte unit of `data` (device, `bytes` a
+ * multiple of 16, 16-byte aligned) once: n_wg workgroups of 256 threads
+ * stride over it with eight non-temporal 16-byte loads in flight per thread
+ * and XOR each thread's words into out[thread] (device uint32, n_wg * 256
+ * values, written).  Asynchronous on `stream`.  Returns 0, -1 for a bad
+ * argument, -5 for a misaligned pointer, -6 if the launch failed. */
+int lcsi_ceiling_read(const void *data, size_t bytes, uint32_t *out, int n_wg, void *stream);
 
 #ifdef __cplusplus
 }

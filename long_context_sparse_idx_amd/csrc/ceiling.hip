@@ -1,5 +1,6 @@
-// Measurement helper (not a step of the method): the practical ceiling of
-// the indexer score kernel's matrix-core work on this chip.  A loop issues
+// Measurement helpers (not steps of the method): the practical ceiling of
+// the indexer score kernel's matrix-core work on this chip, and of a plain
+// streaming read from HBM (the roof of the memory-bound decode kernels).  A loop issues
 // the score kernel's instruction stream -- per 32-key block and wave, 16
 // v_mfma_f32_32x32x16_bf16 in two accumulator chains (two 32-row tiles of
 // (query, head) rows against the block's keys, 8 k-steps of 16 dims) -- at
@@ -94,9 +95,38 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2)))
     if (lane == 0) out[(size_t)blockIdx.x * NWAVE + wave] = sum;
 }
 
+// Streaming read: every 16-byte unit of the buffer once (grid-stride, eight
+// loads in flight per thread, non-temporal), XOR-reduced to one word per
+// thread so no load is dead.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4 *p, size_t n16, uint32_t *out)
+{
+    constexpr int U = 8;
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (size_t)gridDim.x * blockDim.x;
+    u32x4 acc{0, 0, 0, 0};
+    size_t i = tid;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+    out[tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
 
 extern "C" {
+
+int lcsi_ceiling_read(const void *data, size_t bytes, uint32_t *out, int n_wg, void *stream)
+{
+    if (!data || !out || n_wg < 1 || bytes < 16 || bytes % 16) return -1;
+    if (((uintptr_t)data % 16) || ((uintptr_t)out % 4)) return -5;
+    hipLaunchKernelGGL(read_kernel, dim3(n_wg), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const u32x4 *>(data), bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 size_t lcsi_ceiling_data_elems(void) { return (size_t)64 * NWAVE * 64 * 128 + 2 * KT * 128; }
 
