@@ -1,6 +1,7 @@
 """The counter summaries behind the benchmark's `hbm` block
 (long_context_sparse_idx_amd/counters.py) on synthetic rocprofv3 databases,
-and bench.py's lookup of an entry by kernel and source hash.  CPU only."""
+bench.py's lookup of an entry by kernel and source hash, and bench.py's
+refusal of a multi-GPU run.  CPU only."""
 import hashlib
 import json
 import os
@@ -107,3 +108,13 @@ def test_bench_uses_an_entry_only_while_its_sources_match(tmp_profiles, monkeypa
     entry["sources"]["attn.hip"] = "0" * 64   # measured on other sources
     path.write_text(json.dumps({"entries": [entry]}))
     assert bench.counter_entry("wl", "attn_kernel") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py --gpus N with N > 1 exits with a message (the library has no
+    multi-GPU mode); checked before anything touches a GPU."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
