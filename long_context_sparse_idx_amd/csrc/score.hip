@@ -31,9 +31,18 @@
 //   A (Q):  lane holds row (lane % 32), 8 consecutive k-slots of group g
 //   B (K):  lane holds column (lane % 32), the same 8 k-slots of group g
 //   D:      lane holds column (lane % 32), rows 8*(r/4) + 4*g + (r%4), r < 16
-// The d index behind k-slot e of group g in k-step s is g*D/2 + 8*s + e: both
-// operands use the same map, so the MFMA still sums all D products, and each
-// lane reads one contiguous half of a row (128 B for D = 128).
+// Both operands use the same map from (group g, k-step s, k-slot e) to the d
+// index, so the MFMA still sums all D products:
+//   bf16 keys:  d = 16*s + 8*g + e  -- the two lanes of one key read adjacent
+//               16-byte chunks, so one load instruction of a wave touches 32
+//               bytes of each of its 32 keys (the split-key kernel reads its
+//               keys straight from memory this way: half the distinct cache
+//               lines per instruction of the split-halves map, 9 % less time
+//               at 131K keys);
+//   fp8 keys (widened to bf16): d = g*D/2 + 8*s + e -- each lane reads one
+//               contiguous half of the key row (64 B for D = 128).
+// Every kernel of one key format uses the same map, so their scores are
+// bit-identical.
 #include <type_traits>
 
 #include "device_common.h"
@@ -61,8 +70,9 @@ struct KeyGeom {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Q fragments and per-row weights of one wave (64 rows = 64/H queries).
-template <int H, int D>
+// Q fragments and per-row weights of one wave (64 rows = 64/H queries); ILV:
+// the interleaved d map of bf16 keys (else the split-halves map).
+template <int H, int D, bool ILV>
 struct WaveRows {
     bf16x8 qa[2][KeyGeom<D>::KSTEPS];
     float wl[2][16];
@@ -75,9 +85,9 @@ struct WaveRows {
             const int row = rt * 32 + l32;
             const int t = tq0 + row / H, h = row % H;
             if (t < a.T_q) {
-                const uint8_t *base = a.q + b * a.q_sb + (int64_t)t * a.q_st + h * a.q_sh + g * KeyGeom<D>::HALF * 2;
+                const uint8_t *base = a.q + b * a.q_sb + (int64_t)t * a.q_st + h * a.q_sh + g * (ILV ? 16 : KeyGeom<D>::HALF * 2);
 #pragma unroll
-                for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(ld16(base + 16 * s));
+                for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(ld16(base + (ILV ? 32 : 16) * s));
             } else {
 #pragma unroll
                 for (int s = 0; s < KeyGeom<D>::KSTEPS; ++s) qa[rt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
@@ -358,6 +368,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     using G = KeyGeom<D>;
     constexpr bool Q8 = F == F_QK8;
     constexpr bool DMA = F != F_K8;
+    constexpr bool ILV = F == F_BF16;                  // interleaved d map
     constexpr int QPW = 64 / H;
     constexpr int QPB = WAVES_PREFILL * QPW;
     constexpr int NT = WAVES_PREFILL * 64;
@@ -397,7 +408,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
         }
     }
 
-    typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D>>::type rows;
+    typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D, ILV>>::type rows;
     const int tq0 = t0 + wave * QPW;
     rows.load(a, b, tq0, lane);
 
@@ -415,7 +426,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
     // scheduling barrier, so the VALU work of one wave fills the MFMA
     // pipeline's shadow whatever the surrounding control flow.
     auto block = [&](const uint8_t *tb, int cb, float ksc, int key, auto &sink) {
-        const uint8_t *src = tb + (cb * 32 + l32) * ROWB + g * G::HALF * (Q8 ? 1 : 2);
+        const uint8_t *src = tb + (cb * 32 + l32) * ROWB + g * (Q8 ? G::HALF : (ILV ? 16 : G::HALF * 2));
         f32x16 acc0 = f32x16{0}, acc1 = f32x16{0};
         EpiAcc<H> ea;
         ea.init();
@@ -438,7 +449,7 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
             constexpr int NMF = 2 * G::KSTEPS, UPM = 32 / NMF;
             bf16x8 bk[G::KSTEPS];
 #pragma unroll
-            for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 16 * s));
+            for (int s = 0; s < G::KSTEPS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(src + (ILV ? 32 : 16) * s));
 #pragma unroll
             for (int i = 0; i < NMF; ++i) {
                 if (i % 2 == 0)
@@ -674,6 +685,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     using G = KeyGeom<D>;
     constexpr bool Q8 = F == F_QK8;
     constexpr bool K8 = F != F_BF16;
+    constexpr bool ILV = !K8;  // interleaved d map
     constexpr int QPW = 64 / H;
     // per lane: G::HALF key elements = HALF*2 bytes (bf16) or HALF bytes (fp8)
     constexpr int NLD = K8 ? G::HALF / 16 : G::HALF / 8;  // 16-byte loads per lane per block
@@ -695,7 +707,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     if (key_lo >= key_hi) return;
     const int nblk = (int)((key_hi - key_lo + 31) / 32);
 
-    typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D>>::type rows;
+    typename std::conditional<Q8, WaveRows8<H, D>, WaveRows<H, D, ILV>>::type rows;
     rows.load(a, b, tq0, lane);
     const uint8_t *kb = a.k + b * a.k_sb;
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
@@ -719,7 +731,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     const uint32_t sstride = 3 * WAVES_SPLIT * 32 * 4;
     auto fetch = [&](uint32_t &koff, uint32_t &soff, u32x4 (&r)[NLD], float &sc) {
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) r[i] = ld16_ranged(kr, kr_bytes, koff + 16 * i);
+        for (int i = 0; i < NLD; ++i) r[i] = ld16_ranged(kr, kr_bytes, koff + (ILV ? 32 : 16) * i);
         if constexpr (K8) sc = ld4_ranged(sr, sr_bytes, soff);
         koff += kstride;
         soff += sstride;
@@ -757,7 +769,7 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     };
 
     int blk = wave;
-    const uint32_t kgo = g * (K8 ? G::HALF : G::HALF * 2);
+    const uint32_t kgo = g * (K8 ? G::HALF : 16);
     uint32_t ko0 = (uint32_t)(blk * 32 + l32) * (uint32_t)a.k_st + kgo, so0 = (uint32_t)(blk * 32 + l32) * 4;
     uint32_t ko1 = ko0 + (uint32_t)(WAVES_SPLIT * 32) * (uint32_t)a.k_st, so1 = so0 + WAVES_SPLIT * 32 * 4;
     uint32_t ko2 = ko1 + (uint32_t)(WAVES_SPLIT * 32) * (uint32_t)a.k_st, so2 = so1 + WAVES_SPLIT * 32 * 4;
