@@ -178,6 +178,22 @@ __device__ __forceinline__ u32x4 ld16_ranged(const void *base, uint32_t bytes, u
 #endif
 }
 
+// ld16_ranged with the non-temporal hint: for data read once, in whole cache
+// lines per load instruction.
+__device__ __forceinline__ u32x4 ld16_ranged_nt(const void *base, uint32_t bytes, uint32_t off)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000),
+                                         (int)off, 0, 2));
+#else
+    (void)base;
+    (void)bytes;
+    (void)off;
+    return u32x4{0, 0, 0, 0};
+#endif
+}
+
 __device__ __forceinline__ float ld4_ranged(const void *base, uint32_t bytes, uint32_t off)
 {
 #if defined(__HIP_DEVICE_COMPILE__)

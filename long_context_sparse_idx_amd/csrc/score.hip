@@ -54,6 +54,17 @@ namespace {
 
 constexpr int WAVES_PREFILL = 8;  // 512 threads: 2 waves per SIMD
 constexpr int WAVES_SPLIT = 4;
+// Split-key kernel: register buffers per wave (the blocks in flight plus the
+// one computing) and the waves per SIMD the register allocation must allow
+// (1: no limit), per key format.  At 131K bf16 / 1M fp8 keys with 64 heads,
+// three buffers at two waves per SIMD were best; four to eight buffers at
+// one wave per SIMD lost 3-17 %, and fp8 keys without the two-wave bound
+// (more registers, one wave) lost 9 %.
+constexpr int SPLIT_NB_BF16 = 3, SPLIT_OCC_BF16 = 1;
+constexpr int SPLIT_NB_F8 = 3, SPLIT_OCC_F8 = 2;
+// workgroups a split-key call aims for: two per CU in one round (with 256,
+// one per CU, 1M fp8 keys took 30 % longer)
+constexpr int SPLIT_WGS = 512;
 
 // Operand formats: bf16 keys and queries; fp8 keys widened to bf16; fp8
 // keys and fp8 queries on fp8 MFMA.
@@ -676,11 +687,18 @@ __global__ __launch_bounds__(WAVES_PREFILL * 64) void score_prefill_kernel(Score
 // ---------------------------------------------------------------------------
 // Split-key variant for few query rows (decode): a workgroup takes one group
 // of 64/H query rows and a contiguous key range; its 4 waves stride over the
-// 32-key blocks of that range, reading key fragments straight from HBM with
-// the next block's loads in flight while the current block computes.
+// 32-key blocks of that range, each block read from HBM in whole key rows
+// (load i of a block gives lane l the 16-byte chunk l % CPR of key
+// RPL*i + l / CPR: every load instruction covers RPL consecutive rows, with
+// the non-temporal hint, as the keys are read once) two blocks ahead of the
+// compute.  A wave turns a block into its B fragments through its own LDS
+// tile (row-major, rows padded by 16 bytes: conflict-free in both
+// directions), so no barrier is needed.  (Loads that give each lane its own
+// key directly touch 32 keys' cache lines per instruction instead of RPL
+// rows': 12 % slower at 131K keys.)
 // ---------------------------------------------------------------------------
-template <int H, int D, int F>
-__global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreArgs a)
+template <int H, int D, int F, int NB, int OCC>
+__global__ __launch_bounds__(WAVES_SPLIT * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void score_splitkey_kernel(ScoreArgs a)
 {
     using G = KeyGeom<D>;
     constexpr bool Q8 = F == F_QK8;
@@ -689,6 +707,12 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     constexpr int QPW = 64 / H;
     // per lane: G::HALF key elements = HALF*2 bytes (bf16) or HALF bytes (fp8)
     constexpr int NLD = K8 ? G::HALF / 16 : G::HALF / 8;  // 16-byte loads per lane per block
+    constexpr int ROWK = K8 ? D : 2 * D;                   // bytes per key row
+    constexpr int CPR = ROWK / 16;                         // 16-byte chunks per key row
+    constexpr int RPL = 64 / CPR;                          // key rows per load instruction
+    constexpr int ROWP = ROWK + 16;                        // LDS bytes per key row (padded)
+    static_assert(NLD * RPL == 32, "a block is NLD whole-row loads");
+    __shared__ __attribute__((aligned(16))) uint8_t tr[WAVES_SPLIT][32 * ROWP];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
     int b = blockIdx.z;
@@ -713,11 +737,11 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     float *Sb = a.S + (int64_t)b * a.T_q * a.ld;
     const RowSpan rs{Sb + (int64_t)tq0 * a.ld, (uint32_t)((min(a.T_q, tq0 + QPW) - tq0) * a.ld * 4), a.ld, tq0};
 
-    // three register buffers: the blocks two and one steps ahead are in
-    // flight while the current one computes (the loop is unrolled by three so
-    // the buffers rotate by name, without copies)
-    u32x4 r0[NLD], r1[NLD], r2[NLD];
-    float s0 = 1.f, s1 = 1.f, s2 = 1.f;
+    // NB register buffers: the blocks NB-1 .. 1 steps ahead are in flight
+    // while the current one computes (the loop is unrolled by NB, so the
+    // buffers rotate by compile-time index, without copies)
+    u32x4 r[NB][NLD];
+    float sc[NB];
     // keys key_lo .. key_hi-1 through range-checked buffer loads: blocks and
     // keys past the range read as zeros without a branch
     const uint8_t *kr = kb + key_lo * a.k_st;
@@ -727,18 +751,33 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     // Each buffer keeps its own running byte offsets (advanced by three
     // blocks per use), so the load addresses live in registers of their own
     // and never share one with a load still in flight.
-    const uint32_t kstride = (uint32_t)(3 * WAVES_SPLIT * 32) * (uint32_t)a.k_st;
-    const uint32_t sstride = 3 * WAVES_SPLIT * 32 * 4;
-    auto fetch = [&](uint32_t &koff, uint32_t &soff, u32x4 (&r)[NLD], float &sc) {
+    const uint32_t kstride = (uint32_t)(NB * WAVES_SPLIT * 32) * (uint32_t)a.k_st;
+    const uint32_t sstride = NB * WAVES_SPLIT * 32 * 4;
+    const uint32_t rstep = (uint32_t)RPL * (uint32_t)a.k_st;  // bytes between a block's loads
+    auto fetch = [&](uint32_t &koff, uint32_t &soff, u32x4 (&rb)[NLD], float &sb) {
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) r[i] = ld16_ranged(kr, kr_bytes, koff + (ILV ? 32 : 16) * i);
-        if constexpr (K8) sc = ld4_ranged(sr, sr_bytes, soff);
+        for (int i = 0; i < NLD; ++i) rb[i] = ld16_ranged_nt(kr, kr_bytes, koff + rstep * i);
+        if constexpr (K8) sb = ld4_ranged(sr, sr_bytes, soff);
         koff += kstride;
         soff += sstride;
     };
-    auto step = [&](int blk, const u32x4 (&cur)[NLD], float cs, u32x4 (&ahead)[NLD], float &as, uint32_t &koff,
+    // the block's chunks through this wave's LDS tile: written as loaded,
+    // read back as this lane's key (l32) and k-slot chunks -- chunk 2i + g
+    // (bf16, the interleaved map) or g*CPR/2 + i (fp8, split halves)
+    uint8_t *tw = tr[wave];
+    auto to_lanes = [&](const u32x4 (&ld)[NLD], u32x4 (&x)[NLD]) {
+        uint8_t *wp = tw + (lane / CPR) * ROWP + 16 * (lane % CPR);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) st16(wp + RPL * ROWP * i, ld[i]);
+        const uint8_t *rp = tw + l32 * ROWP;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) x[i] = ld16(rp + 16 * (ILV ? 2 * i + g : g * (CPR / 2) + i));
+    };
+    auto step = [&](int blk, const u32x4 (&ld)[NLD], float cs, u32x4 (&ahead)[NLD], float &as, uint32_t &koff,
                     uint32_t &soff) {
         fetch(koff, soff, ahead, as);
+        u32x4 cur[NLD];
+        to_lanes(ld, cur);
         f32x16 acc0, acc1;
         if constexpr (Q8) {
             i32x8 bk[G::KSTEPS8];
@@ -769,18 +808,26 @@ __global__ __launch_bounds__(WAVES_SPLIT * 64) void score_splitkey_kernel(ScoreA
     };
 
     int blk = wave;
-    const uint32_t kgo = g * (K8 ? G::HALF : 16);
-    uint32_t ko0 = (uint32_t)(blk * 32 + l32) * (uint32_t)a.k_st + kgo, so0 = (uint32_t)(blk * 32 + l32) * 4;
-    uint32_t ko1 = ko0 + (uint32_t)(WAVES_SPLIT * 32) * (uint32_t)a.k_st, so1 = so0 + WAVES_SPLIT * 32 * 4;
-    uint32_t ko2 = ko1 + (uint32_t)(WAVES_SPLIT * 32) * (uint32_t)a.k_st, so2 = so1 + WAVES_SPLIT * 32 * 4;
-    fetch(ko0, so0, r0, s0);
-    fetch(ko1, so1, r1, s1);
-    for (; blk < nblk; blk += 3 * WAVES_SPLIT) {
-        step(blk, r0, s0, r2, s2, ko2, so2);
-        if (blk + WAVES_SPLIT >= nblk) break;
-        step(blk + WAVES_SPLIT, r1, s1, r0, s0, ko0, so0);
-        if (blk + 2 * WAVES_SPLIT >= nblk) break;
-        step(blk + 2 * WAVES_SPLIT, r2, s2, r1, s1, ko1, so1);
+    const uint32_t lbase = (uint32_t)(lane / CPR) * (uint32_t)a.k_st + 16u * (uint32_t)(lane % CPR);
+    // each buffer keeps its own running byte offsets (advanced by NB blocks
+    // per use), so the load addresses live in registers of their own and
+    // never share one with a load still in flight
+    uint32_t ko[NB], so[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        ko[u] = (uint32_t)((blk + u * WAVES_SPLIT) * 32) * (uint32_t)a.k_st + lbase;
+        so[u] = (uint32_t)((blk + u * WAVES_SPLIT) * 32 + l32) * 4;
+        sc[u] = 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) fetch(ko[u], so[u], r[u], sc[u]);
+    for (; blk < nblk; blk += NB * WAVES_SPLIT) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (u > 0 && blk + u * WAVES_SPLIT >= nblk) break;
+            const int nx = (u + NB - 1) % NB;  // the buffer consumed by the previous step
+            step(blk + u * WAVES_SPLIT, r[u], sc[u], r[nx], sc[nx], ko[nx], so[nx]);
+        }
     }
 }
 
@@ -804,7 +851,10 @@ hipError_t launch_score_hd(const ScoreArgs &a, bool split, hipStream_t st)
         const int64_t n_keys = a.q_pos0 + a.T_q;
         dim3 grid((unsigned)((n_keys + a.key_split - 1) / a.key_split), (a.T_q + QPW - 1) / QPW, a.B);
         if (a.rlist) grid = dim3(grid.x, a.rmax, 1);
-        hipLaunchKernelGGL((score_splitkey_kernel<H, D, F>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
+        if constexpr (F == F_BF16)
+            hipLaunchKernelGGL((score_splitkey_kernel<H, D, F, SPLIT_NB_BF16, SPLIT_OCC_BF16>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
+        else
+            hipLaunchKernelGGL((score_splitkey_kernel<H, D, F, SPLIT_NB_F8, SPLIT_OCC_F8>), grid, dim3(WAVES_SPLIT * 64), 0, st, a);
     }
     return hipGetLastError();
 }
@@ -858,7 +908,7 @@ int score_key_split(const ScoreArgs &a)
     // keep ranges a multiple of 256 keys
     const int64_t n_keys = a.q_pos0 + a.T_q;
     const int64_t groups = (int64_t)a.B * ((a.T_q + 64 / a.H - 1) / (64 / a.H));
-    int64_t splits = (512 + groups - 1) / groups;
+    int64_t splits = (SPLIT_WGS + groups - 1) / groups;
     int64_t ks = (n_keys + splits - 1) / splits;
     ks = ((ks + 255) / 256) * 256;
     if (ks < 512) ks = 512;
