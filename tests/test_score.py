@@ -196,6 +196,37 @@ def test_prefill_and_splitkey_kernels_agree_bitwise(fmt, T_kv):
         assert np.array_equal(i1[0, 0], i_all[0, t])
 
 
+@pytest.mark.parametrize("shape", [(3, 1, 9001, 9000, 2048),      # decode rows: split-key kernel
+                                   (1, 512, 4100, 3588, 256)])     # prefill kernel
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_padded_key_rows_score_like_packed_rows(fmt, shape):
+    """Keys whose rows sit in a wider buffer (row stride D + 48 bytes' worth
+    of elements, the padding filled with 0x7F bytes: a huge bf16 value, an
+    fp8 NaN) score and select bit for bit like the same keys packed: every
+    kernel reads a key row's D elements and nothing past them."""
+    B, T_q, T_kv, q_pos0, k = shape
+    H, D = 64, 128
+    log(f"[score-padded] shape={shape} fmt={fmt}")
+    base = inputs.WORKLOADS[{"bf16": "prefill200k", "k8": "prefill1m", "qk8": "prefill1m_q8"}[fmt]]
+    wl = dataclasses.replace(base, name="padded", B=B, T_q=T_q, n_q=T_q, q_pos0=q_pos0, T_kv=T_kv,
+                             H_I=H, D_I=D, top_k=k)
+    x = {n: (v.cuda() if v is not None else None) for n, v in inputs.indexer_inputs(wl, 0, "cpu").items()}
+    S_p, i_p = gpu_indexer(x["q"], x["k"], x["w"], k, q_pos0, k_scale=x["k_scale"], q_scale=x["q_scale"])
+    pad = 48 // x["k"].element_size()
+    if x["k"].element_size() == 1:
+        wide = torch.full((B, T_kv, D + pad), 0x7F, dtype=torch.uint8, device="cuda").view(x["k"].dtype)
+    else:
+        wide = torch.full((B, T_kv, D + pad), 0x7F7F, dtype=torch.int16, device="cuda").view(x["k"].dtype)
+    wide[..., :D] = x["k"]
+    kv = wide[..., :D]
+    assert kv.stride(1) == D + pad
+    S_w, i_w = gpu_indexer(x["q"], kv, x["w"], k, q_pos0, k_scale=x["k_scale"], q_scale=x["q_scale"])
+    for t in range(T_q):
+        n = q_pos0 + t + 1
+        assert np.array_equal(S_w[:, t, :n], S_p[:, t, :n]), f"t={t}: scores differ"
+    assert np.array_equal(i_w, i_p)
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_degenerate_rows(fmt):
     """One key (T_kv = 1) and very short causal rows mixing n <= k and n > k:
