@@ -176,8 +176,9 @@ def measured_ceilings():
     """Practical ceilings on this GPU, for context beside the datasheet peaks:
     a library bf16 GEMM (8192^3, entries N(0,1)/8 like the indexer inputs),
     the score kernel's MFMA stream alone (libceiling.so), a 4 GiB
-    device-to-device copy, a 4 GiB read-only reduction (torch) and a 4 GiB
-    plain streaming read (libceiling.so).  All run after the timed region."""
+    device-to-device copy, a 4 GiB read-only reduction (torch), a 4 GiB
+    plain streaming read and a gather of one decode attention layer's rows
+    (libceiling.so).  All run after the timed region."""
     g = torch.Generator(device="cuda").manual_seed(0)
     n = 8192
     a = (torch.randn(n, n, device="cuda", generator=g) / 8).to(torch.bfloat16)
@@ -222,6 +223,7 @@ def measured_ceilings():
                 "read_4GiB_sum_GBps": round(read, 1), "read_frac_of_peak": round(read / PEAK_HBM_GBS, 4),
                 "read_4GiB_stream_GBps": round(stream_read, 1),
                 "read_stream_frac_of_peak": round(stream_read / PEAK_HBM_GBS, 4)})
+    res.update(gather_ceiling())
     return res
 
 
@@ -251,6 +253,49 @@ def read_ceiling(buf: torch.Tensor) -> float:
     e1.record(stream)
     torch.cuda.synchronize()
     return nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+
+def gather_ceiling() -> dict:
+    """The sparse attention's memory pattern without its arithmetic
+    (libceiling.so): the rows of one decode131k attention layer -- 32
+    sequences x 2048 distinct random rows of 1152 bytes out of 131073 each,
+    every row gathered once -- copied into LDS by 512 workgroups (two per
+    CU) of four 32-row lists, one list in flight while the last is read back."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_idx_amd", "libceiling.so"))
+    lib.lcsi_ceiling_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lcsi_ceiling_gather.restype = ctypes.c_int
+    B, N, k, rowb = 32, 131073, 2048, 1152
+    kv = torch.empty(B * N * rowb // 4, dtype=torch.int32, device="cuda")  # contents do not matter
+    g = torch.Generator(device="cuda").manual_seed(1)
+    rows = torch.stack([torch.randperm(N, generator=g, device="cuda")[:k].sort().values + b * N
+                        for b in range(B)]).to(torch.int32).contiguous()   # [B, k] global row numbers
+    n_wg, tiles = B * k // 128, 4
+    out = torch.empty(n_wg * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.lcsi_ceiling_gather(ctypes.c_void_p(kv.data_ptr()), B * N, rowb, ctypes.c_void_p(rows.data_ptr()),
+                                     n_wg, tiles, ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"lcsi_ceiling_gather: {rc}")
+    for _ in range(2):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del kv, rows, out
+    torch.cuda.empty_cache()
+    gbs = B * k * rowb / (ms / 1e3) / 1e9
+    return {"gather_1152B_rows_decode131k_us": round(ms * 1e3, 2), "gather_1152B_rows_GBps": round(gbs, 1),
+            "gather_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def split_ms(events, nchunk, L):
@@ -324,6 +369,11 @@ def secondary(name: str, steps: int, warmup: int):
         q_b = wl.D_I * (1 if wl.q_fp8 else 2) + (8 if wl.q_fp8 else 4)
         nbytes = wl.B * (wl.T_kv * (key_b + 4) + wl.H_I * q_b) * sum(wl.pattern)
         out["score_algorithmic_GBps_evented"] = round(nbytes / (sc / 1e3) / 1e9, 1)
+        # attention: the gathered KV rows of every layer over the evented
+        # step's attention time (the split partials and Q/O not counted)
+        kv_b = wl.B * min(wl.top_k, wl.T_kv) * (2 * wl.D_qk) * L
+        out["attention_us_per_layer_evented"] = round(at / L * 1e3, 2)
+        out["attention_algorithmic_GBps_evented"] = round(kv_b / (at / 1e3) / 1e9, 1)
     log(f"[bench] {name}: {ms:.3f} ms/step ({out[unit]:.0f} {unit}), all-F {ms_f:.3f} ms, "
         f"x{out['speedup_vs_allF']} ({time.time() - t0:.1f} s)")
     del path
@@ -521,6 +571,11 @@ def main():
         if wl.T_q > 1 and not wl.q_fp8:
             ceil = extra["measured_ceilings"]["mfma_lds_reads_TFLOPs"]
             roofline["frac_of_mfma_lds_ceiling"] = round(roofline["achieved"] / ceil, 4)
+        # (the gather ceiling is measured on the decode131k layer's shape)
+        if "decode131k" in extra:
+            extra["decode131k"]["attention_frac_of_gather_ceiling"] = round(
+                extra["decode131k"]["attention_algorithmic_GBps_evented"] /
+                extra["measured_ceilings"]["gather_1152B_rows_GBps"], 4)
         log(f"[bench] ceilings: {extra['measured_ceilings']}")
 
     line = {

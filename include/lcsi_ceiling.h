@@ -1,8 +1,9 @@
 /*
  * lcsi_ceiling.h -- measurement helpers of the benchmark, in their own
  * library (libceiling.so), not steps of the method: the practical
- * matrix-core ceiling of the indexer score kernel on this GPU, and the
- * practical rate of a plain streaming read from HBM.
+ * matrix-core ceiling of the indexer score kernel on this GPU, the
+ * practical rate of a plain streaming read from HBM, and that of a gather
+ * of whole rows into LDS (the sparse attention's memory pattern).
  *
  * lcsi_ceiling_mfma launches n_wg workgroups of 8 waves (two per SIMD, as
  * the score kernel) that each issue `blocks` times the score kernel's block
@@ -41,6 +42,21 @@ int lcsi_ceiling_mfma(const uint16_t *data, float *out, int n_wg, int blocks, in
  * values, written).  Asynchronous on `stream`.  Returns 0, -1 for a bad
  * argument, -5 for a misaligned pointer, -6 if the launch failed. */
 int lcsi_ceiling_read(const void *data, size_t bytes, uint32_t *out, int n_wg, void *stream);
+
+/* lcsi_ceiling_gather copies whole rows into LDS the way the sparse
+ * attention kernel gathers its KV rows, without the attention's arithmetic:
+ * n_wg workgroups of 256 threads; workgroup w takes `tiles` (1..64) lists of
+ * 32 row numbers, idx[(w * tiles + t) * 32 + r] (device int32, clamped to
+ * [0, n_rows)), and copies each list's 32 rows of `row_bytes` bytes (16..1152,
+ * a multiple of 16) from rows + number * row_bytes (device, 16-byte aligned)
+ * into LDS with direct 16-byte loads, one list in flight while the previous
+ * one is read back.  Thread i of workgroup w XORs the four words of LDS
+ * 16-byte unit i of every list (chunk i % (row_bytes/16) of row
+ * i / (row_bytes/16)) into out[w * 256 + i] (device uint32, written).
+ * Asynchronous on `stream`.  Returns 0, -1 for a bad argument, -5 for a
+ * misaligned pointer, -6 if the launch failed. */
+int lcsi_ceiling_gather(const void *rows, int64_t n_rows, uint32_t row_bytes, const int32_t *idx, int n_wg,
+                        int tiles, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

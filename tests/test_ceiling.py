@@ -3,9 +3,10 @@
 Host side (no GPU): the library exports every function the header declares
 and refuses bad arguments before launching anything.  GPU: the MFMA loop
 computes the products it claims (each wave's output is the sum of all its
-accumulators, which has a closed form on the CPU), and the streaming read
+accumulators, which has a closed form on the CPU), the streaming read
 touches every 16-byte unit exactly once (its XOR per thread, checked on the
-CPU)."""
+CPU), and the gather lands every listed row's chunks where the read-back
+expects them (clamped row numbers included)."""
 import ctypes
 import os
 import re
@@ -32,13 +33,16 @@ def lib():
     L.lcsi_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
     L.lcsi_ceiling_read.restype = ctypes.c_int
+    L.lcsi_ceiling_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.lcsi_ceiling_gather.restype = ctypes.c_int
     return L
 
 
 def test_exports_every_declared_function():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = set(re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}()]*\)\s*;", text))
-    assert names == {"lcsi_ceiling_data_elems", "lcsi_ceiling_mfma", "lcsi_ceiling_read"}
+    assert names == {"lcsi_ceiling_data_elems", "lcsi_ceiling_mfma", "lcsi_ceiling_read", "lcsi_ceiling_gather"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     assert names <= exported
@@ -57,6 +61,16 @@ def test_bad_arguments_are_refused_before_launch():
     assert L.lcsi_ceiling_read(ctypes.c_void_p(FAKE), 16, ctypes.c_void_p(FAKE), 0, None) == -1
     assert L.lcsi_ceiling_read(ctypes.c_void_p(FAKE + 4), 16, ctypes.c_void_p(FAKE), 1, None) == -5
     assert L.lcsi_ceiling_read(ctypes.c_void_p(FAKE), 16, ctypes.c_void_p(FAKE + 2), 1, None) == -5
+    G = L.lcsi_ceiling_gather
+    F = ctypes.c_void_p(FAKE)
+    assert G(None, 10, 1152, F, 1, 1, F, None) == -1
+    assert G(F, 0, 1152, F, 1, 1, F, None) == -1            # no rows
+    assert G(F, 10, 1160, F, 1, 1, F, None) == -1           # row longer than 1152 bytes
+    assert G(F, 10, 24, F, 1, 1, F, None) == -1             # not whole 16-byte chunks
+    assert G(F, 10, 1152, F, 1, 65, F, None) == -1          # more than 64 lists
+    assert G(F, 10, 1152, F, 0, 1, F, None) == -1
+    assert G(ctypes.c_void_p(FAKE + 8), 10, 1152, F, 1, 1, F, None) == -5
+    assert G(F, 10, 1152, ctypes.c_void_p(FAKE + 2), 1, 1, F, None) == -5
 
 
 NWAVE, ROWS, DIM = 8, 64, 128   # waves per workgroup, query rows per wave, dims
@@ -125,3 +139,35 @@ def test_streaming_read_touches_every_unit_once():
     for t in range(S):
         want[t] = np.bitwise_xor.reduce(per_unit[t::S])
     assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("row_bytes,tiles", [(1152, 5), (256, 2)])
+def test_gather_lands_every_listed_row(row_bytes, tiles):
+    """Thread i of workgroup w XORs LDS unit i of each of its lists: chunk
+    i % cpr of list entry i // cpr (cpr = row_bytes / 16), i.e. 16 bytes of
+    row idx[w, t, i // cpr] (clamped to the rows present).  Some row numbers
+    are out of range on purpose: -3 and n_rows + 5 read rows 0 and n_rows - 1."""
+    L = lib()
+    n_rows, n_wg = 700, 6
+    g = torch.Generator().manual_seed(13)
+    host = torch.randint(0, 2 ** 31 - 1, (n_rows * row_bytes // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    idx = torch.randint(0, n_rows, (n_wg, tiles, 32), generator=g, dtype=torch.int64).to(torch.int32)
+    idx[0, 0, 0], idx[1, tiles - 1, 3] = -3, n_rows + 5
+    rows, didx = host.cuda(), idx.cuda()
+    out = torch.zeros(n_wg * 256, dtype=torch.int32, device="cuda")
+    rc = L.lcsi_ceiling_gather(ctypes.c_void_p(rows.data_ptr()), n_rows, row_bytes, ctypes.c_void_p(didx.data_ptr()),
+                               n_wg, tiles, ctypes.c_void_p(out.data_ptr()),
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    words = host.numpy().view(np.uint32).reshape(n_rows, row_bytes // 16, 4)
+    unit = words[:, :, 0] ^ words[:, :, 1] ^ words[:, :, 2] ^ words[:, :, 3]
+    cpr = row_bytes // 16
+    cl = np.clip(idx.numpy(), 0, n_rows - 1)
+    want = np.zeros((n_wg, 256), np.uint32)
+    for w in range(n_wg):
+        for t in range(tiles):
+            for i in range(256):
+                want[w, i] ^= unit[cl[w, t, i // cpr], i % cpr]
+    assert np.array_equal(out.cpu().numpy().view(np.uint32).reshape(n_wg, 256), want)
