@@ -7,6 +7,9 @@
         -> per-kernel average of every counter in the runs, as a markdown table
     python -m long_context_sparse_idx_amd.counters trace OUT_MD TITLE COMMAND DB
         -> per-kernel calls, total and average duration of a --kernel-trace run
+    python -m long_context_sparse_idx_amd.counters mfma OUT_MD TITLE COMMAND DB
+        -> MFMA instructions, flops and busy cycles per kernel, with the clock
+           and busy fraction they imply
 
 Each database is the output of one ``rocprofv3 --pmc ... -- python3 bench.py
 ... --calibrate-copy`` run.  HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per
@@ -179,6 +182,45 @@ def trace(out_md: str, title: str, command: str, db_path: str):
     print(f"wrote {out_md}")
 
 
+def mfma(out_md: str, title: str, command: str, db_path: str, n_simd: int = 1024, n_xcd: int = 8):
+    """One counter pass of SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_BF16,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE: the SQ
+    counters are summed over all SIMDs, GRBM_GUI_ACTIVE over the XCDs, MOPS
+    count 512 flops each.  The clock is one XCD's active cycles over the
+    dispatch's duration in the same run (kernels run slower under counter
+    collection)."""
+    pd = per_dispatch(db_path)
+    db = sqlite3.connect(db_path)
+    dur = defaultdict(list)
+    try:
+        for name, start, end in db.execute("select name, start, end from kernels"):
+            dur[short_name(name)].append((end - start) / 1e6)
+    except sqlite3.Error:
+        pass
+    mean = lambda v: sum(v) / len(v) if v else 0.0
+    with open(out_md, "w") as fh:
+        fh.write(f"# {title}\n\nCommand, from the repository root:\n\n```\n{command}\n```\n\n")
+        fh.write(f"Per-dispatch averages over {n_simd} SIMDs and {n_xcd} XCDs.\n\n"
+                 "| kernel | dispatches | avg ms | MFMA instructions | MFMA flops (MOPS x 512) | "
+                 "MFMA busy cycles / SIMD | active cycles / XCD | clock (GHz) | MFMA busy |\n"
+                 "|---|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+        for name, cs in sorted(pd.items(), key=lambda kv: -mean(dur.get(short_name(kv[0]), []))):
+            sn = short_name(name)
+            if not any(sn.startswith(k) for k in KERNEL_SOURCES):
+                continue
+            n = max(len(v) for v in cs.values())
+            ms = mean(dur.get(sn, []))
+            ins = mean(cs.get("SQ_INSTS_VALU_MFMA_BF16", []))
+            flops = mean(cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])) * 512
+            busy = mean(cs.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / n_simd
+            act = mean(cs.get("GRBM_GUI_ACTIVE", [])) / n_xcd
+            # (no clock for dispatches too short for their duration to mean much)
+            clock = f"{act / (ms * 1e-3) / 1e9:.2f}" if ms >= 0.01 and act > 0 and busy > 0 else "--"
+            frac = f"{100 * busy / act:.0f} %" if act > 0 and busy > 0 else ("0 %" if act > 0 else "--")
+            fh.write(f"| `{sn}` | {n} | {ms:.3f} | {ins:.4g} | {flops:.4g} | {busy:.4g} | {act:.4g} | {clock} | {frac} |\n")
+    print(f"wrote {out_md}")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "hbm":
         hbm(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -186,6 +228,8 @@ if __name__ == "__main__":
         table(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     elif len(sys.argv) == 6 and sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif len(sys.argv) == 6 and sys.argv[1] == "mfma":
+        mfma(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     else:
         print(__doc__)
         sys.exit(2)

@@ -118,3 +118,17 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_mfma_summary_derives_clock_and_busy_fraction(tmp_profiles):
+    """Busy cycles per SIMD over active cycles per XCD, and the clock from
+    the active cycles over the dispatch's duration."""
+    K = "void lcsi::(anonymous namespace)::score_prefill_kernel<64, 128, 0, true>(lcsi::ScoreArgs)"
+    db = make_db(tmp_profiles / "m.db", [
+        (1, K, "SQ_INSTS_VALU_MFMA_BF16", 4.0e8), (1, K, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2.0e10),
+        (1, K, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1.5e7), (1, K, "GRBM_GUI_ACTIVE", 8 * 2.0e7)],
+        kernels=[(K, 0, 10_000_000)])   # 10 ms
+    out = tmp_profiles / "mfma.md"
+    counters.mfma(str(out), "title", "cmd", str(db))
+    text = out.read_text()
+    assert "| `score_prefill_kernel<64, 128, 0, true>` | 1 | 10.000 | 4e+08 | 1.024e+13 | 1.5e+07 | 2e+07 | 2.00 | 75 % |" in text
