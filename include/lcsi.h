@@ -217,7 +217,7 @@ int sparse_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
  * LCSI_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
  * until the process ends (looked up on the first call per device).  A call
  * whose sparse_attn workspace requirement exceeds it returns LCSI_ESCRATCH
- * (at H_q = 64, D_v = 512, top_k = 2048: up to 45 sequences) and launches
+ * (at H_q = 64, D_v = 512, top_k = 2048: more than 95 sequences) and launches
  * nothing; LCSI_EINVAL also when `stream` belongs to another device than the
  * current one.  The call allocates nothing.  Every call on one GPU uses that
  * GPU's one scratch: calls that overlap on one GPU (other streams, other
@@ -243,13 +243,24 @@ int sparse_attn_noalloc(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb,
  *              n_slots = 1 reuses one buffer for every F layer (no extra
  *              memory); n_slots = #F keeps every F layer's set.
  *   ws / ws_bytes  one workspace for all steps (they run in order on one
- *              stream); query mode returns the largest single requirement.
+ *              stream); query mode returns what the group needs: the largest
+ *              single requirement, or for a decode group (T_q == 1, whose
+ *              attention splits every index list) the indexer's largest
+ *              requirement plus two attention partial regions (below).
  *   events     optional HOST array of 4*L hipEvent_t (as void*), or NULL.
  *              For layer l: [4l] before the layer, [4l+1] after scoring
  *              (with the fused pass: after it and the two rescoring
  *              launches),
  *              [4l+2] after selection, [4l+3] after attention (for an S
  *              layer the first three are recorded at the same point).
+ * Decode groups: the log-sum-exp merge of layer l's attention parts is done
+ * by the workgroups of layer l+1's attention launch, before their own work
+ * (the last layer's by a merge launch of its own), so no merge launch sits
+ * between two layers; the results are the same bytes as sparse_attn's.  The
+ * parts of consecutive layers alternate between the two partial regions.
+ * Layer l's output is therefore complete only once layer l+1's attention
+ * has run (event [4(l+1)+3]; every output at the end of the group), and no
+ * layer's output may overlap another layer's inputs.
  * Pattern errors return LCSI_EPATTERN before anything is launched. */
 int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
                     int n_idx_args, const lcsi_attn *attn_args,

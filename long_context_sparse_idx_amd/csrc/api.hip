@@ -259,7 +259,11 @@ int run_indexer(const lcsi_indexer *a, int32_t *idx, int64_t idx_sb, int64_t idx
     return LCSI_OK;
 }
 
-int run_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx_st, float *ws, hipStream_t s)
+// `host`: an earlier split call's merge for this launch to do first (or
+// null); `defer`: if not null, a split call leaves its own merge to the
+// caller (in *defer) instead of launching it.
+int run_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx_st, float *ws, hipStream_t s,
+             const MergeArgs *host = nullptr, MergeArgs *defer = nullptr)
 {
     AttnArgs aa{};
     aa.B = a->B;
@@ -298,7 +302,8 @@ int run_attn(const lcsi_attn *a, const int32_t *idx, int64_t idx_sb, int64_t idx
         aa.part_o = (uint16_t *)ws;
         aa.part_ml = (float *)((char *)ws + o);
     }
-    return launch_attn(aa, s) == hipSuccess ? LCSI_OK : LCSI_EHIP;
+    if (host) aa.mg = *host;
+    return launch_attn(aa, s, defer) == hipSuccess ? LCSI_OK : LCSI_EHIP;
 }
 
 constexpr int MAX_DEVICES = 64;
@@ -383,7 +388,7 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
     if (!pattern[0] || nf != n_idx_args) return LCSI_EPATTERN;
     if (!idx_args) return LCSI_EINVAL;
     int rc;
-    size_t need = 0;
+    size_t need = 0, need_attn = 0;
     const lcsi_attn *a0 = &attn_args[0];
     for (int f = 0; f < nf; ++f) {
         const lcsi_indexer *x = &idx_args[f];
@@ -397,8 +402,17 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
         if ((rc = check_attn(y))) return rc;
         if (y->B != a0->B || y->T_q != a0->T_q || y->q_pos0 != a0->q_pos0 || y->top_k != a0->top_k) return LCSI_EINVAL;
         const size_t s = attn_ws_bytes(y);
-        need = s > need ? s : need;
+        need_attn = s > need_attn ? s : need_attn;
     }
+    // Split (decode) attention: a layer's partial results are merged by the
+    // next layer's attention launch (the last layer's by a merge launch of
+    // its own), so two partial regions alternate after the indexer's region.
+    // (All layers share B, T_q and top_k, so all split or none do.)
+    AttnPlan pl0;
+    attn_ws_bytes(a0, &pl0);
+    const bool defer = pl0.splits > 1;
+    const size_t attn_off = defer ? align_ws(need) : 0, attn_reg = align_ws(need_attn);
+    need = defer ? attn_off + 2 * attn_reg : (need > need_attn ? need : need_attn);
     if (!ws && ws_bytes) return workspace_rule(ws, ws_bytes, need) < 0 ? LCSI_EINVAL : LCSI_OK;
     if ((rc = check_idx_out(idx_cache, idx_sb, idx_st))) return rc;
     rc = workspace_rule(ws, ws_bytes, need);
@@ -407,6 +421,7 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
     hipStream_t s = (hipStream_t)stream;
     int f = 0;
     int32_t *cur = nullptr;
+    MergeArgs pending{};  // the previous layer's merge, still to do (S == 0: none)
     for (int l = 0; l < L; ++l) {
         if ((rc = record(events, 4 * l, s))) return rc;
         if (pattern[l]) {
@@ -417,7 +432,16 @@ int run_layer_group(int L, const uint8_t *pattern, const lcsi_indexer *idx_args,
         } else {
             if ((rc = record(events, 4 * l + 1, s)) || (rc = record(events, 4 * l + 2, s))) return rc;
         }
-        if ((rc = run_attn(&attn_args[l], cur, idx_sb, idx_st, ws, s))) return rc;
+        if (defer) {
+            float *pws = (float *)((char *)ws + attn_off + (size_t)(l & 1) * attn_reg);
+            MergeArgs own{};
+            if ((rc = run_attn(&attn_args[l], cur, idx_sb, idx_st, pws, s, pending.S ? &pending : nullptr, &own)))
+                return rc;
+            pending = own;
+            if (l == L - 1 && pending.S && launch_merge(pending, s) != hipSuccess) return LCSI_EHIP;
+        } else if ((rc = run_attn(&attn_args[l], cur, idx_sb, idx_st, ws, s))) {
+            return rc;
+        }
         if ((rc = record(events, 4 * l + 3, s))) return rc;
     }
     return LCSI_OK;

@@ -32,6 +32,10 @@
 // Each wave owns 16 heads and DV/NDS output dims; a workgroup has NWH head
 // groups x NDS dim slices = 4 waves for up to 32 heads, 8 waves for 64 heads
 // (so every variant keeps two waves per SIMD resident).
+// Decode calls split each row's index list; the parts are merged by
+// log-sum-exp either by a merge launch or (MG) by the workgroups of a later
+// attention launch, as a prologue whose loads are in flight together with
+// the first gather.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -85,7 +89,106 @@ __device__ __forceinline__ float max_lane_rows(float x)
     return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
-template <int DQK, int DV, int NWH, int NDS, bool SHARED>
+// ---- Merge of a split call's parts.  With each part's normalised output
+// N_s = O_s / l_s (fp16) and its (m_s, l_s) (fp32, log2 units),
+//   O = sum_s w_s N_s / sum_s w_s,  w_s = l_s 2^(m_s - M),  M = max_s m_s,
+// summed over s in ascending order; parts with no usable key (m_s = -inf)
+// are skipped, and a row with none at all gets zeros.  One thread merges NE
+// consecutive output dims of one (row, head); every thread of every merging
+// kernel does the same arithmetic per element, so the result does not depend
+// on which launch merges.
+constexpr int MAXS = 8;  // parts of a decode row: at most 2048 / 256
+
+template <int NE>
+struct MergeLd {
+    uint32_t o[MAXS][NE / 2];
+    f32x2 ml[MAXS];
+};
+
+// Every part's loads first (parts past S re-read the last one; they are not used).
+template <int NE>
+__device__ __forceinline__ void merge_load(const MergeArgs &m, int64_t row, int h, int d, MergeLd<NE> &x)
+{
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+        const int se = s < m.S ? s : m.S - 1;
+        const int64_t r = (row * m.S + se) * m.H + h;
+        x.ml[s] = *reinterpret_cast<const f32x2 *>(m.part_ml + r * 2);
+        const uint16_t *po = m.part_o + r * m.DV + d;
+        if constexpr (NE == 8) {
+            const u32x4 v = ld16(po);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x.o[s][i] = v[i];
+        } else {
+            static_assert(NE == 4, "4 or 8 dims per thread");
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(po);
+            x.o[s][0] = v[0];
+            x.o[s][1] = v[1];
+        }
+    }
+}
+
+template <int NE>
+__device__ __forceinline__ void merge_store(const MergeArgs &m, int64_t row, int h, int d, const MergeLd<NE> &x)
+{
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s)
+        if (s < m.S) M = fmaxf(M, x.ml[s][0]);
+    float o[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) o[e] = 0.f;
+    float L = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            if (s >= m.S || x.ml[s][0] == -__builtin_inff()) continue;
+            const float w = x.ml[s][1] * __builtin_amdgcn_exp2f(x.ml[s][0] - M);
+            L += w;
+#pragma unroll
+            for (int e = 0; e < NE; e += 2) {
+                o[e] = __builtin_fmaf(f16_lo(x.o[s][e / 2]), w, o[e]);
+                o[e + 1] = __builtin_fmaf(f16_hi(x.o[s][e / 2]), w, o[e + 1]);
+            }
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int b = (int)(row / m.T_q), t = (int)(row % m.T_q);
+    uint16_t *op = m.out + (int64_t)b * m.o_sb + (int64_t)t * m.o_st + (int64_t)h * m.o_sh + d;
+    if constexpr (NE == 8)
+        st16(op, u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)});
+    else
+        *reinterpret_cast<u32x2 *>(op) = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+}
+
+// The share of merge items (row, head) of one workgroup of a launch that
+// hosts another call's merge: items are dealt to the launch's workgroups in
+// contiguous runs; within a workgroup, DV/8 threads merge one item (8 dims
+// each, 16-byte loads), NT threads take NT/(DV/8) items per pass.
+struct MergeShare {
+    int64_t it0, it_end;  // this workgroup's items
+    int ipp, sub, d;      // items per pass; this thread's item in a pass, its first dim
+};
+
+template <int NT>
+__device__ __forceinline__ MergeShare merge_share(const MergeArgs &m)
+{
+    MergeShare sh;
+    const int64_t items = (int64_t)m.rows * m.H;
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+    const int64_t wid = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t per = (items + nwg - 1) / nwg;
+    sh.it0 = wid * per;
+    sh.it_end = min(items, sh.it0 + per);
+    const int tpi = m.DV / 8;
+    sh.ipp = NT / tpi;
+    sh.sub = (int)threadIdx.x / tpi;
+    sh.d = 8 * ((int)threadIdx.x % tpi);
+    return sh;
+}
+
+template <int DQK, int DV, int NWH, int NDS, bool SHARED, bool MG>
 __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnArgs a)
 {
     // Row-major KV tile in LDS: each row holds the K row (DQK bf16) and, when
@@ -202,12 +305,39 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
         }
     };
 
-    const int32_t keys0 = usable(raw_idx(0));
+    const int32_t raw0 = raw_idx(0);
     int32_t raw_next = raw_idx(1);
+    // MG: this workgroup's share of an earlier split call's merge.  The first
+    // pass's loads go out before the first gather and are used while the
+    // gather is in flight; further passes (more items than one pass of the
+    // workgroup takes) follow.
+    MergeShare msh{};
+    MergeLd<8> mld;
+    int64_t m_it = 0;
+    if constexpr (MG) {
+        msh = merge_share<64 * NW>(a.mg);
+        m_it = msh.it0 + msh.sub;
+        // (loaded unconditionally -- a thread without an item re-reads item
+        // 0 and stores nothing -- so no branch makes the compiler wait for
+        // these loads before the gather's index shuffles)
+        const int64_t li = m_it < msh.it_end ? m_it : 0;
+        merge_load<8>(a.mg, li / a.mg.H, (int)(li % a.mg.H), msh.d, mld);
+    }
+    const int32_t keys0 = usable(raw0);
     gather(keys0, kv0);
     uint32_t vmask = (uint32_t)__ballot(keys0 >= 0);  // bit r: tile row r usable
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if constexpr (MG) {
+        // (stored after the wait above: the first tile's wait does not
+        // include these stores)
+        if (m_it < msh.it_end) merge_store<8>(a.mg, m_it / a.mg.H, (int)(m_it % a.mg.H), msh.d, mld);
+        for (m_it += msh.ipp; m_it - msh.sub < msh.it_end; m_it += msh.ipp) {
+            if (m_it >= msh.it_end) continue;
+            merge_load<8>(a.mg, m_it / a.mg.H, (int)(m_it % a.mg.H), msh.d, mld);
+            merge_store<8>(a.mg, m_it / a.mg.H, (int)(m_it % a.mg.H), msh.d, mld);
+        }
+    }
     // tile `it` computes from `tb` while tile it+1 is gathered into `nb`
     auto step = [&](int it, const uint8_t *tb, uint8_t *nb) {
         const int32_t keys_next = usable(raw_next);
@@ -339,69 +469,21 @@ __global__ __launch_bounds__(64 * NWH * NDS) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// Combine the per-split partial results of one (query row, head): with
-// each part's normalised output N_s = O_s / l_s,
-// O = sum_s w_s N_s / sum_s w_s,  w_s = l_s 2^(m_s - M),  M = max_s m_s,
-// summed over s in ascending order.  One workgroup per (head, row); thread i
-// owns output dims 4i .. 4i+3.  S = the split count, fixed at compile time so
-// that every partial of a thread is loaded before the first is used.
-template <int S>
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
+// The merge as a launch of its own: one workgroup per (head, row), thread i
+// merges output dims 4i .. 4i+3.
+__global__ __launch_bounds__(128) void attn_merge_kernel(MergeArgs m)
 {
     const int h = blockIdx.x;
     const int64_t row = blockIdx.y;  // b * T_q + t
-    const int b = (int)(row / a.T_q), t = (int)(row % a.T_q);
     const int d = 4 * threadIdx.x;
-    if (d >= a.DV) return;
-    float ms[S], ls[S];
-    f32x4 os[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int64_t r = (row * S + s) * a.H + h;
-        const f32x2 ml = *reinterpret_cast<const f32x2 *>(a.part_ml + r * 2);
-        ms[s] = ml[0];
-        ls[s] = ml[1];
-        const u32x2 hv = *reinterpret_cast<const u32x2 *>(a.part_o + r * a.DV + d);
-        os[s] = f32x4{f16_lo(hv.x), f16_hi(hv.x), f16_lo(hv.y), f16_hi(hv.y)};
-    }
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ms[s]);
-    f32x4 o{0, 0, 0, 0};
-    float L = 0.f;
-    if (M != -__builtin_inff()) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            if (ms[s] == -__builtin_inff()) continue;
-            const float ws = ls[s] * __builtin_amdgcn_exp2f(ms[s] - M);
-            L += ws;
-            o += os[s] * ws;
-        }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    o *= inv;
-    uint16_t *op = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + d;
-    *reinterpret_cast<u32x2 *>(op) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    if (d >= m.DV) return;
+    MergeLd<4> x;
+    merge_load<4>(m, row, h, d, x);
+    merge_store<4>(m, row, h, d, x);
 }
 
-hipError_t launch_merge(const AttnArgs &a, hipStream_t st)
-{
-    const dim3 grid(a.H, a.B * a.T_q), block(128);
-    switch (a.splits) {
-    case 2: hipLaunchKernelGGL(attn_merge_kernel<2>, grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL(attn_merge_kernel<3>, grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL(attn_merge_kernel<4>, grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL(attn_merge_kernel<5>, grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL(attn_merge_kernel<6>, grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL(attn_merge_kernel<7>, grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL(attn_merge_kernel<8>, grid, block, 0, st, a); break;
-    default: return hipErrorInvalidValue;  // (a decode call has at most 2048 / 256 parts)
-    }
-    return hipGetLastError();
-}
-
-template <int DQK, int DV, bool SHARED>
-hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
+template <int DQK, int DV, bool SHARED, bool MG>
+hipError_t launch_attn_k(const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(a.splits * a.hgroups, a.T_q, a.B);
     const int nwh = ((a.H + 15) / 16 + a.hgroups - 1) / a.hgroups;  // 16-head groups per workgroup
@@ -413,22 +495,44 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st)
             // (not planned for separate 576/512 K and V rows: a wave's share
             // of the gather map would spill)
             if constexpr (SHARED || DQK != 576)
-                hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 2, SHARED>), grid, dim3(128), 0, st, a);
+                hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 2, SHARED, MG>), grid, dim3(128), 0, st, a);
             else
                 return hipErrorInvalidValue;
         } else {
-            hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED, MG>), grid, dim3(256), 0, st, a);
         }
     } else if (nwh == 1) {
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 4, SHARED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 1, 4, SHARED, MG>), grid, dim3(256), 0, st, a);
     } else if (nwh == 2) {
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 2, 2, SHARED, MG>), grid, dim3(256), 0, st, a);
     } else {
-        hipLaunchKernelGGL((attn_kernel<DQK, DV, 4, 2, SHARED>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((attn_kernel<DQK, DV, 4, 2, SHARED, MG>), grid, dim3(512), 0, st, a);
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+template <int DQK, int DV, bool SHARED>
+hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st, MergeArgs *defer)
+{
+    hipError_t e = a.mg.S > 1 ? launch_attn_k<DQK, DV, SHARED, true>(a, st) : launch_attn_k<DQK, DV, SHARED, false>(a, st);
     if (e != hipSuccess || a.splits == 1) return e;
-    return launch_merge(a, st);
+    MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_ml = a.part_ml;
+    m.out = a.out;
+    m.o_sb = a.o_sb;
+    m.o_st = a.o_st;
+    m.o_sh = a.o_sh;
+    m.rows = a.B * a.T_q;
+    m.T_q = a.T_q;
+    m.H = a.H;
+    m.DV = a.DV;
+    m.S = a.splits;
+    if (defer) {
+        *defer = m;
+        return hipSuccess;
+    }
+    return launch_merge(m, st);
 }
 
 }  // namespace
@@ -459,7 +563,14 @@ AttnPlan attn_plan(int B, int T_q, int H, int DQK, int top_k)
     return pl;
 }
 
-hipError_t launch_attn(const AttnArgs &a_in, hipStream_t st)
+hipError_t launch_merge(const MergeArgs &m, hipStream_t st)
+{
+    if (m.S < 2 || m.S > MAXS || !(m.DV == 512 || m.DV == 128)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(m.H, m.rows), dim3(128), 0, st, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs &a_in, hipStream_t st, MergeArgs *defer)
 {
     AttnArgs a = a_in;
     // one gathered row serves K and V when V is the first D_v columns of the
@@ -476,10 +587,11 @@ hipError_t launch_attn(const AttnArgs &a_in, hipStream_t st)
         const int64_t rows = (int64_t)a.B * a.T_q;
         while (a.hgroups < 4 && 2 * a.hgroups <= gmax && rows * a.splits * a.hgroups < ATTN_WG_TARGET) a.hgroups *= 2;
     }
+    if (a.mg.S > 1 && (a.mg.S > MAXS || !(a.mg.DV == 512 || a.mg.DV == 128))) return hipErrorInvalidValue;
     if (a.DQK == 576 && a.DV == 512)
-        return shared ? launch_attn_d<576, 512, true>(a, st) : launch_attn_d<576, 512, false>(a, st);
+        return shared ? launch_attn_d<576, 512, true>(a, st, defer) : launch_attn_d<576, 512, false>(a, st, defer);
     if (a.DQK == 128 && a.DV == 128)
-        return shared ? launch_attn_d<128, 128, true>(a, st) : launch_attn_d<128, 128, false>(a, st);
+        return shared ? launch_attn_d<128, 128, true>(a, st, defer) : launch_attn_d<128, 128, false>(a, st, defer);
     return hipErrorInvalidValue;
 }
 

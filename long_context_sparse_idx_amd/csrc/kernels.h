@@ -77,6 +77,16 @@ struct SelectArgs {
     const int32_t *ccnt;
 };
 
+// The log-sum-exp merge of one split attention call's partial results
+// (part_o, part_ml as AttnArgs lays them out) into its bf16 output.
+struct MergeArgs {
+    const uint16_t *part_o;
+    const float *part_ml;
+    uint16_t *out;
+    int64_t o_sb, o_st, o_sh;
+    int rows, T_q, H, DV, S;  // rows = B * T_q; S = splits (0: nothing to merge)
+};
+
 struct AttnArgs {
     int B, T_q, T_kv, H, DQK, DV, top_k;
     float sm_scale_log2;      // sm_scale * log2(e)
@@ -96,6 +106,8 @@ struct AttnArgs {
     int hgroups;              // workgroups sharing one row's heads (each takes H / hgroups of them)
     uint16_t *part_o;         // [B*T_q][splits][H][DV] fp16, the part's O / l (splits > 1)
     float *part_ml;           // [B*T_q][splits][H][2]
+    MergeArgs mg;             // another (earlier) split call's merge, done by this launch's workgroups
+                              // before their own work (mg.S == 0: none)
 };
 
 // How sparse_attn splits each row's index list.  The split count (and so the
@@ -135,7 +147,11 @@ struct OverlapArgs {
     int32_t *counts;          // [B * T_q]
 };
 
-hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
+// Launches the attention kernel and, for a split call, its merge -- unless
+// `defer` is set: then the merge is left to the caller (MergeArgs of this
+// call in *defer), who hands it to a later launch's `mg` or to launch_merge.
+hipError_t launch_attn(const AttnArgs &a, hipStream_t st, MergeArgs *defer = nullptr);
+hipError_t launch_merge(const MergeArgs &m, hipStream_t st);
 hipError_t launch_overlap(const OverlapArgs &a, hipStream_t st);
 
 }  // namespace lcsi

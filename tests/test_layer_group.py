@@ -197,3 +197,42 @@ def test_leading_s_layer_is_rejected():
     with pytest.raises(lcsi.LcsiError) as e:
         run_group(wl, (0, 1, 0, 0), f_dev, a_dev, n_slots=1)
     assert e.value.code == lcsi.LCSI_EPATTERN
+
+
+@pytest.mark.parametrize("name,B,heads", [("decode131k", 32, (64, 64, 40, 64, 64, 24, 64, 48)),
+                                          ("decode1m", 8, (64,) * 12),
+                                          ("decode131k", 3, (16, 64, 33, 64, 8, 64, 64, 17))])
+def test_decode_group_outputs_equal_standalone_calls(name, B, heads):
+    """In a decode group each layer's split-attention merge is done by the next
+    layer's attention launch (the last layer's by a merge launch): every
+    layer's output must equal a standalone sparse_attn call on the same
+    inputs and index set byte for byte, also where neighbouring layers have
+    different head counts (so the launch that merges has another grid than
+    the layer it merges)."""
+    base = inputs.WORKLOADS[name]
+    wl = dataclasses.replace(base, B=B, q_pos0=9000, T_kv=9001)
+    log(f"[group] {name} B={B} heads={heads}: deferred merges vs standalone calls")
+    f_in, a_in = build(wl)
+    f_dev = [to_dev(x) for x in f_in]
+    a_dev = [attn_dev(x) for x in a_in]
+    L = len(wl.pattern)
+    # per-layer head counts: a prefix of the workload's query heads
+    outs = [torch.full((B, 1, h, wl.D_v), float("nan"), dtype=torch.bfloat16, device="cuda") for h in heads]
+    tau = inputs.sm_scale(wl)
+    ids = [lcsi.indexer_desc(x["q"], x["k"], x["w"], wl.top_k, wl.q_pos0, k_scale=x["k_scale"]) for x in f_dev]
+    ads = [lcsi.attn_desc(a_dev[l]["q"][:, :, :heads[l]], a_dev[l]["k"], a_dev[l]["v"], outs[l], wl.top_k,
+                          wl.q_pos0, tau) for l in range(L)]
+    nf = len(f_dev)
+    cache = torch.full((nf, B, 1, wl.top_k), -9, dtype=torch.int32, device="cuda")
+    lcsi.run_layer_group(wl.pattern, ids, ads, cache, nf, B * wl.top_k, wl.top_k, wl.top_k)
+    torch.cuda.synchronize()
+    fi = -1
+    for l, is_f in enumerate(wl.pattern):
+        fi += 1 if is_f else 0
+        ref = torch.empty_like(outs[l])
+        lcsi.sparse_attn(lcsi.attn_desc(a_dev[l]["q"][:, :, :heads[l]], a_dev[l]["k"], a_dev[l]["v"], ref,
+                                        wl.top_k, wl.q_pos0, tau), cache[fi])
+        torch.cuda.synchronize()
+        assert not torch.isnan(outs[l].float()).any(), f"layer {l}: output not written"
+        assert torch.equal(outs[l].view(torch.int16), ref.view(torch.int16)), f"layer {l}"
+    log(f"  {L} layers byte-identical")
