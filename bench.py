@@ -335,6 +335,40 @@ def time_steps(path, plan, steps, warmup):
     return ms, sc, se, at
 
 
+def decode_graph(path, plan, steps):
+    """A decode step as one HIP graph replay against eager launches: steps
+    back to back (throughput), and one token at a time with the host waiting
+    for each step (the latency a decode loop that samples between tokens
+    sees, where the host's launch rate can fall behind short kernels)."""
+    B = path.wl.B
+    g = path.capture(plan)
+    g.replay()
+    torch.cuda.synchronize()
+
+    def per_token(fn):
+        ts = []
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return float(np.median(ts))
+
+    e0, e1 = _events(2)
+    e0.record(torch.cuda.current_stream())
+    for _ in range(steps):
+        g.replay()
+    e1.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / steps
+    lat_eager = per_token(lambda: path.step(plan))
+    lat_graph = per_token(g.replay)
+    del g
+    return {"graph_ms_per_step": round(ms_graph, 4), "graph_tok/s": round(B / (ms_graph / 1e3), 1),
+            "token_latency_ms_eager": round(lat_eager, 4), "token_latency_ms_graph": round(lat_graph, 4),
+            "token_latency_note": "host clock around one step plus a synchronize, median of the timed steps"}
+
+
 def secondary(name: str, steps: int, warmup: int):
     """One of the other workloads, its layer pattern against all-F."""
     wl = inputs.WORKLOADS[name]
@@ -374,6 +408,7 @@ def secondary(name: str, steps: int, warmup: int):
         kv_b = wl.B * min(wl.top_k, wl.T_kv) * (2 * wl.D_qk) * L
         out["attention_us_per_layer_evented"] = round(at / L * 1e3, 2)
         out["attention_algorithmic_GBps_evented"] = round(kv_b / (at / 1e3) / 1e9, 1)
+        out.update(decode_graph(path, pat, steps))
     log(f"[bench] {name}: {ms:.3f} ms/step ({out[unit]:.0f} {unit}), all-F {ms_f:.3f} ms, "
         f"x{out['speedup_vs_allF']} ({time.time() - t0:.1f} s)")
     del path

@@ -100,3 +100,13 @@ class Workload:
         for c, (q0, tq, T_kv, ids, ads, cache) in enumerate(plans):
             lcsi.run_layer_group(pattern, ids, ads, cache, self.n_slots, self.slot_stride, self.idx_sb,
                                  self.idx_st, ws=self.ws, events=events[c] if events is not None else None)
+
+    def capture(self, plan):
+        """One step recorded as a HIP graph (torch.cuda.CUDAGraph): replaying
+        it re-issues every launch of the step with one host call.  The step
+        must have run eagerly once before (workspace, kernel loading).  Only
+        kernels are captured (the library issues no memset or copy)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(plan)
+        return g
