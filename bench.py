@@ -58,6 +58,22 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def counter_entries(workload: str, kernel_prefix: str):
+    """Every committed FETCH_SIZE / WRITE_SIZE entry of this workload whose
+    kernel name starts with kernel_prefix (all template variants), or None
+    when there is none or a source one was taken from has changed since."""
+    try:
+        with open(COUNTERS_JSON) as f:
+            doc = json.load(f)
+    except OSError:
+        return None
+    es = [e for e in doc.get("entries", [])
+          if e["workload"] == workload and e["kernel"].startswith(kernel_prefix)]
+    if not es or not all(source_sha(s) == h for e in es for s, h in e["sources"].items()):
+        return None
+    return es
+
+
 def counter_entry(workload: str, kernel_prefix: str, kernel_suffix: str = ""):
     """The committed FETCH_SIZE / WRITE_SIZE entry of a kernel (HBM bytes per
     launch), or None when there is none for this workload or a source it was
@@ -545,14 +561,16 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     def hbm_stage(primary, others, stage_ms):
-        """A stage of several kernels (select chain, attention + merge): its
-        bytes per call = the counted bytes of all its kernels over the calls
-        of its first kernel, against the stage's time per call here."""
-        e0 = counter_entry(wl.name, primary)
-        if e0 is None:
+        """A stage of the path (selection, attention with its merges): its
+        bytes per call = the counted bytes of every kernel of the stage (all
+        template variants of each name) over the calls in the counted run
+        (one launch of a `primary` kernel per call), against the stage's time
+        per call here."""
+        ps = counter_entries(wl.name, primary)
+        if ps is None:
             return None
-        parts = [e0] + [e for e in (counter_entry(wl.name, o) for o in others) if e is not None]
-        total = sum(e["bytes_per_launch"] * e["dispatches"] for e in parts) / e0["dispatches"]
+        parts = ps + [e for o in others for e in (counter_entries(wl.name, o) or [])]
+        total = sum(e["bytes_per_launch"] * e["dispatches"] for e in parts) / sum(e["dispatches"] for e in ps)
         gbs = total / (stage_ms / 1e3) / 1e9
         return {"kernels": [e["kernel"] for e in parts], "bytes_per_call": int(total),
                 "call_ms_this_run": round(stage_ms, 4), "GBps": round(gbs, 1),
