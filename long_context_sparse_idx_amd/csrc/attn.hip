@@ -542,11 +542,14 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t st, MergeArgs *defer)
 #endif
 #ifndef ATTN_WG_TARGET
 // Workgroups a decode call aims for by sharing out heads.  Every workgroup
-// sharing a row's heads gathers the row's KV rows again (from L2 at best):
-// at 32 rows x 8 parts one 64-head workgroup per part (256 workgroups, one
-// per CU) beat two 32-head workgroups per part (512) by ~3 % (31.9-32.3 vs
-// 32.8-33.4 us per decode131k layer, kernel trace, same machine).
-#define ATTN_WG_TARGET 256
+// sharing a row's heads gathers the row's KV rows again (from L2 at best),
+// which costs more than leaving CUs idle, down to about half the chip
+// (kernel traces, one machine per comparison): at 32 rows x 8 parts one
+// 64-head workgroup per part (256 workgroups) beat two 32-head ones (512),
+// 31.9-32.3 vs 32.8-33.4 us per decode131k layer; at 8 rows x 8 parts two
+// 32-head workgroups per part (128) beat four 16-head ones (256) and one
+// 64-head one (64): 21.0-21.4 vs 22.9-23.4 and 26.9 us per decode1m layer.
+#define ATTN_WG_TARGET 128
 #endif
 
 AttnPlan attn_plan(int B, int T_q, int H, int DQK, int top_k)
