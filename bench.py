@@ -74,6 +74,23 @@ def counter_entries(workload: str, kernel_prefix: str):
     return es
 
 
+def hbm_stage_for(workload: str, primary: str, others, stage_ms: float):
+    """A stage of the path (score, selection, attention with its merges): its
+    HBM bytes per call = the counted bytes of every kernel of the stage (all
+    template variants of each name) over the calls in the counted run (one
+    launch of a `primary` kernel per call), against the stage's time per call
+    measured in this run; None without a current counter entry."""
+    ps = counter_entries(workload, primary)
+    if ps is None or stage_ms <= 0:
+        return None
+    parts = ps + [e for o in others for e in (counter_entries(workload, o) or [])]
+    total = sum(e["bytes_per_launch"] * e["dispatches"] for e in parts) / sum(e["dispatches"] for e in ps)
+    gbs = total / (stage_ms / 1e3) / 1e9
+    return {"kernels": [e["kernel"] for e in parts], "bytes_per_call": int(total),
+            "call_ms_this_run": round(stage_ms, 4), "GBps": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def counter_entry(workload: str, kernel_prefix: str, kernel_suffix: str = ""):
     """The committed FETCH_SIZE / WRITE_SIZE entry of a kernel (HBM bytes per
     launch), or None when there is none for this workload or a source it was
@@ -424,6 +441,15 @@ def secondary(name: str, steps: int, warmup: int):
         kv_b = wl.B * min(wl.top_k, wl.T_kv) * (2 * wl.D_qk) * L
         out["attention_us_per_layer_evented"] = round(at / L * 1e3, 2)
         out["attention_algorithmic_GBps_evented"] = round(kv_b / (at / 1e3) / 1e9, 1)
+        # measured HBM traffic per call (committed counter runs of the same
+        # sources) over the evented step's time per call
+        n_f = sum(wl.pattern)
+        out["hbm"] = {
+            "source": "bytes per call from profiles/hbm_counters.json; call times from this run's evented step",
+            "score": hbm_stage_for(name, "score_splitkey_kernel", (), sc / n_f),
+            "select": hbm_stage_for(name, "select_filter_kernel", ("select_final_kernel",), se / n_f),
+            "attention": hbm_stage_for(name, "attn_kernel", ("attn_merge_kernel",), at / L),
+        }
         out.update(decode_graph(path, pat, steps))
     log(f"[bench] {name}: {ms:.3f} ms/step ({out[unit]:.0f} {unit}), all-F {ms_f:.3f} ms, "
         f"x{out['speedup_vs_allF']} ({time.time() - t0:.1f} s)")
@@ -561,20 +587,7 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     def hbm_stage(primary, others, stage_ms):
-        """A stage of the path (selection, attention with its merges): its
-        bytes per call = the counted bytes of every kernel of the stage (all
-        template variants of each name) over the calls in the counted run
-        (one launch of a `primary` kernel per call), against the stage's time
-        per call here."""
-        ps = counter_entries(wl.name, primary)
-        if ps is None:
-            return None
-        parts = ps + [e for o in others for e in (counter_entries(wl.name, o) or [])]
-        total = sum(e["bytes_per_launch"] * e["dispatches"] for e in parts) / sum(e["dispatches"] for e in ps)
-        gbs = total / (stage_ms / 1e3) / 1e9
-        return {"kernels": [e["kernel"] for e in parts], "bytes_per_call": int(total),
-                "call_ms_this_run": round(stage_ms, 4), "GBps": round(gbs, 1),
-                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        return hbm_stage_for(wl.name, primary, others, stage_ms)
     select_ms_call = float(np.mean(select_ms)) / (nchunk * n_f)
     hbm_block = {
         "source": "bytes per launch from profiles/hbm_counters.json (rocprofv3 FETCH_SIZE and WRITE_SIZE "

@@ -110,6 +110,31 @@ def test_bench_uses_an_entry_only_while_its_sources_match(tmp_profiles, monkeypa
     assert bench.counter_entry("wl", "attn_kernel") is None
 
 
+def test_bench_stage_bytes_sum_every_variant_per_call(tmp_profiles, monkeypatch):
+    """A stage's bytes per call: every template variant of its kernels (a
+    decode group's attention launches with and without the previous layer's
+    merge, and its one merge launch) over the calls, one per primary launch."""
+    sys.path.insert(0, ROOT)
+    import bench
+    path = tmp_profiles / "hbm_counters.json"
+    src = {"attn.hip": sha("attn.hip")}
+    es = [{"workload": "wl", "kernel": "attn_kernel<576, 512, 4, 2, true, true>", "dispatches": 7,
+           "bytes_per_launch": 1000, "sources": src},
+          {"workload": "wl", "kernel": "attn_kernel<576, 512, 4, 2, true, false>", "dispatches": 1,
+           "bytes_per_launch": 600, "sources": src},
+          {"workload": "wl", "kernel": "attn_merge_kernel", "dispatches": 1, "bytes_per_launch": 400,
+           "sources": src}]
+    path.write_text(json.dumps({"entries": es}))
+    monkeypatch.setattr(bench, "COUNTERS_JSON", str(path))
+    st = bench.hbm_stage_for("wl", "attn_kernel", ("attn_merge_kernel",), 0.001)
+    assert st["bytes_per_call"] == (7 * 1000 + 600 + 400) // 8
+    assert st["GBps"] == pytest.approx(1000.0 / 1e-6 / 1e9)
+    assert bench.hbm_stage_for("wl", "select_filter_kernel", (), 0.001) is None
+    es[1]["sources"] = {"attn.hip": "0" * 64}   # one variant measured on other sources
+    path.write_text(json.dumps({"entries": es}))
+    assert bench.hbm_stage_for("wl", "attn_kernel", ("attn_merge_kernel",), 0.001) is None
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py --gpus N with N > 1 exits with a message (the library has no
     multi-GPU mode); checked before anything touches a GPU."""
