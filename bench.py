@@ -450,7 +450,11 @@ def secondary(name: str, steps: int, warmup: int):
             "select": hbm_stage_for(name, "select_filter_kernel", ("select_final_kernel",), se / n_f),
             "attention": hbm_stage_for(name, "attn_kernel", ("attn_merge_kernel",), at / L),
         }
-        out.update(decode_graph(path, pat, steps))
+        try:
+            out.update(decode_graph(path, pat, steps))
+        except RuntimeError as e:  # a capture failure must not cost the rest of the line
+            out["graph_error"] = str(e)[:200]
+            torch.cuda.synchronize()
     log(f"[bench] {name}: {ms:.3f} ms/step ({out[unit]:.0f} {unit}), all-F {ms_f:.3f} ms, "
         f"x{out['speedup_vs_allF']} ({time.time() - t0:.1f} s)")
     del path
