@@ -344,6 +344,12 @@ def split_ms(events, nchunk, L):
     return sc, se, at
 
 
+def score_ms_of(events, chunks, L, pattern):
+    """Score ms of the given chunks of one step from run_layer_group's
+    per-layer events (F layers only)."""
+    return sum(events[c][4 * l].elapsed_time(events[c][4 * l + 1]) for c in chunks for l in range(L) if pattern[l])
+
+
 def time_steps(path, plan, steps, warmup):
     """ms per step over `steps` back-to-back steps (no per-layer events), and
     one more step with per-layer events: (ms/step, score ms, select ms,
@@ -509,8 +515,15 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
 
+    # the fused candidate pass (prefill kernel, 16+ heads, a row longer than
+    # its candidate slots): the library plans it when its workspace needs
+    # the slots; chunks of shorter rows run unfused
+    def plan_fused(d):
+        return lcsi.idx_score_topk_ws_bytes(d) > lcsi.idx_score_topk_ws_bytes(d, lcsi.LCSI_UNFUSED)
+    fused_chunks = [c for c, p in enumerate(plans) if plan_fused(p[3][0])] if wl.T_q > 1 else []
+
     start, end = _events(2)
-    step_ms, idx_ms, score_ms, select_ms, attn_ms = [], [], [], [], []
+    step_ms, idx_ms, score_ms, select_ms, attn_ms, fused_ms = [], [], [], [], [], []
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
@@ -519,6 +532,7 @@ def main():
         path.step(plan, events)
         torch.cuda.synchronize()
         sc, se, at = split_ms(events, nchunk, L)
+        fused_ms.append(score_ms_of(events, fused_chunks, L, pattern))
         step_ms.append(s0.elapsed_time(events[-1][-1]))
         score_ms.append(sc)
         select_ms.append(se)
@@ -543,12 +557,7 @@ def main():
     score_s = float(np.mean(score_ms)) / 1e3
     kdt = "fp8xfp8" if wl.q_fp8 else ("fp8" if wl.key_fp8 else "bf16")
 
-    # the fused candidate pass (prefill kernel, 16+ heads, a row longer than
-    # its candidate slots): the library plans it when its workspace needs
-    # the slots; chunks of shorter rows run unfused
-    def plan_fused(d):
-        return lcsi.idx_score_topk_ws_bytes(d) > lcsi.idx_score_topk_ws_bytes(d, lcsi.LCSI_UNFUSED)
-    n_fused = sum(plan_fused(p[3][0]) for p in plans)
+    n_fused = len(fused_chunks)
     fused = n_fused > 0
     peak = PEAK_FP8_TFLOPS if wl.q_fp8 else PEAK_BF16_TFLOPS
     score_launch_ms = float(np.mean(score_ms)) / (nchunk * n_f)
@@ -556,11 +565,22 @@ def main():
     score_counters = (counter_entry(wl.name, "score_prefill_kernel", ", true>" if fused else ", false>")
                       if wl.T_q > 1 else counter_entry(wl.name, "score_splitkey_kernel"))
     if wl.T_q > 1:
-        achieved = pairs * flops_per_pair * n_f / score_s / 1e12
+        # the dominant kernel's own launches: the fused chunks where there are
+        # any (their algorithmic flops over their score time: the launch with
+        # its zeroing and rescoring launches, ~15 us of a ~10 ms chunk)
+        dom = fused_chunks if fused else list(range(nchunk))
+        pairs_dom = sum(pairs_in_chunk(plans[c][0], plans[c][1]) for c in dom) * wl.B
+        dom_s = (float(np.mean(fused_ms)) if fused else float(np.mean(score_ms))) / 1e3
+        achieved = pairs_dom * flops_per_pair * n_f / dom_s / 1e12
+        all_achieved = pairs * flops_per_pair * n_f / score_s / 1e12
+        score_launch_ms = dom_s * 1e3 / (len(dom) * n_f)
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": score_counters["bytes_per_launch"] if score_counters else None,
-                    "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}{',fused' if fused else ''}>"}
+                    "kernel": f"score_prefill_kernel<{wl.H_I},{wl.D_I},{kdt}{',fused' if fused else ''}>",
+                    "all_chunks": {"achieved": round(all_achieved, 2), "frac": round(all_achieved / peak, 4),
+                                   "avg_chunk_ms": round(score_s * 1e3 / (nchunk * n_f), 4),
+                                   "note": "every chunk's score phase, the short unfused first chunks included"}}
     else:
         # keys (+ fp8 scale) read once per sequence, queries and weights, score row written
         key_b = wl.D_I * (1 if wl.key_fp8 else 2) + (4 if wl.key_fp8 else 0)
@@ -571,9 +591,9 @@ def main():
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": score_counters["bytes_per_launch"] if score_counters else None,
                     "kernel": f"score_splitkey_kernel<{wl.H_I},{wl.D_I},{kdt}>"}
-    roofline["launches_per_step"] = nchunk * n_f
+    roofline["launches_per_step"] = (n_fused if fused else nchunk) * n_f
     if fused:
-        roofline["fused_launches_per_step"] = n_fused * n_f
+        roofline["unfused_launches_per_step"] = (nchunk - n_fused) * n_f
     roofline["avg_launch_ms"] = round(score_launch_ms, 4)
     # attention: bytes of the gathered KV rows (576 x bf16 per selected index) + Q + O
     sel_per_row = sum(min(wl.top_k, p + 1) for p in range(wl.q_pos0, wl.q_pos0 + wl.n_q)) * wl.B
